@@ -1,0 +1,202 @@
+/*
+ * pa.h -- C ABI of libpa: single-query decode attention over a block-paged
+ * KV cache on AMD Instinct MI355X (gfx950), plus the host block allocator
+ * that produces its block tables and slot mappings.
+ *
+ * What the operations are (the pages on PagedAttention this follows):
+ *  - The KV cache is cut into fixed-size physical blocks that need not be
+ *    adjacent; a request takes a new block only when its current one is
+ *    full ("Paged attention in LLMs", section "The fix").
+ *  - Each request owns a block table mapping logical block j to a physical
+ *    block; attention follows the table to each block in turn, so the
+ *    sequence reads in order although storage is scattered (same page,
+ *    "Keeping track: the block table").  Position pos lives in block
+ *    table[pos / block_size] at offset pos % block_size (PagedAttention MCQ
+ *    page, code sketch).
+ *  - The attention itself is standard scaled dot-product attention over the
+ *    gathered keys and values; only storage changes ("Paged Attention",
+ *    chapter introduction; MCQ page, code sketch), and real kernels fold the
+ *    table lookup into their tile loop (MCQ page, code sketch).
+ *  - Requests with a common prefix point their own tables at the same
+ *    blocks ("Paged attention in LLMs", "Sharing blocks"); a shared block is
+ *    copied on write (MCQ page, comparison table, beam search / best of N).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are hipMalloc'd (or torch) device memory owned by the
+ *    caller, who keeps them alive until the stream work completes.  The
+ *    library keeps no pointer after a call returns, allocates no device
+ *    memory and never synchronises the stream.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *  - Every argument is validated on the host before anything is enqueued;
+ *    a call that returns an error has enqueued nothing.  A launch failure
+ *    reported by the runtime returns PA_ERR_LAUNCH.
+ *  - Device data is range-checked where a bad value could address memory
+ *    outside a buffer: a slot outside the pool is skipped by the writes; a
+ *    block-table entry outside [0, num_blocks) or a sequence longer than its
+ *    table turns that sequence's output rows into NaN.  Nothing faults.
+ *
+ * Device layout of one layer's cache (the pages keep keys and values of a
+ * (block, kv-head) pair as [block_size][head_dim]; here the same tile is
+ * stored in the order the gfx950 matrix cores consume it).  With
+ * X = 16 / sizeof(element) (8 for bf16, 4 for f32) and head_dim % X == 0:
+ *    k_cache: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *    v_cache: [num_blocks][num_kv_heads][head_dim][block_size]
+ * The key of the token in slot s (block s / bs, offset s % bs), kv-head h,
+ * dimension d is k_cache[s/bs][h][d/X][s%bs][d%X]; its value is
+ * v_cache[s/bs][h][d][s%bs].  A (block, head) tile is contiguous
+ * (block_size * head_dim elements for each of K and V).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size */
+    PA_ERR_UNSUPPORTED = 2, /* a shape or dtype the kernels are not built for */
+    PA_ERR_OOM = 3,         /* allocator: not enough free blocks (state unchanged) */
+    PA_ERR_NOT_FOUND = 4,   /* allocator: unknown sequence id */
+    PA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a launch */
+    PA_ERR_EXISTS = 6       /* allocator: sequence id already in use */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(pa_status status);
+
+/* ------------------------------------------------------------------------
+ * Cache append: write each new token's keys and values into its slot.
+ * The cache grows by one token per decode step and each token lands in the
+ * slot its request's block table gives it ("Paged attention in LLMs",
+ * "The cache being stored"; MCQ page, code sketch).
+ *
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim], dtype, contiguous
+ *   slot_mapping  device, int64 [num_tokens]; token t goes to slot
+ *                 slot_mapping[t] = block * block_size + offset.  A negative
+ *                 slot means "skip this token"; a slot >= num_blocks *
+ *                 block_size is skipped as well.  Slots of one call must be
+ *                 distinct (two tokens writing one slot race).
+ *   k_cache, v_cache  device, the layout above; only the named slots change.
+ *   head_dim      64 or 128;  block_size 8, 16 or 32;  num_tokens >= 0.
+ * ------------------------------------------------------------------------ */
+pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
+                         void* k_cache, void* v_cache,
+                         int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Copy whole physical blocks (keys and values of every kv-head): the copy
+ * of a shared, partially filled block made before a request writes into it
+ * (MCQ page, comparison table, "Copy on write blocks").
+ *
+ *   pairs   device, int32 [num_pairs][2] = (source block, destination block).
+ *           Pairs with a block outside [0, num_blocks) are skipped.  No
+ *           destination may also be a source or another pair's destination.
+ * ------------------------------------------------------------------------ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention: for every sequence b and query head h,
+ *   out[b][h] = softmax_p(scale * q[b][h] . K[p][g]) . V[p][g],  p in [0, L_b)
+ * with g = h / (num_q_heads / num_kv_heads) and K[p], V[p] read through the
+ * block table (block block_tables[b][p / bs], offset p % bs).  L_b counts
+ * the token being decoded (write it with pa_cache_write first).  L_b = 0
+ * gives a zero row.  Entries of a table row past ceil(L_b / bs) are never
+ * read, nor is any slot at or past L_b.
+ *
+ *   q             device, [num_seqs][num_q_heads][head_dim], dtype
+ *   k_cache, v_cache  device, the layout above, [num_blocks] blocks
+ *   block_tables  device, int32 [num_seqs][max_blocks_per_seq], row-major
+ *   seq_lens      device, int32 [num_seqs]
+ *   out           device, [num_seqs][num_q_heads][head_dim], dtype (rounded
+ *                 to nearest-even from float32 for bf16)
+ *   num_q_heads % num_kv_heads == 0 and num_q_heads / num_kv_heads <= 16.
+ *   dtype PA_BF16: bf16 inputs, bf16 matrix-core products, float32
+ *   accumulation and softmax.  PA_F32: float32 throughout.
+ *
+ * Long contexts (split-sequence decode): with partition_size > 0 each
+ * sequence is cut into partitions of partition_size tokens (a multiple of
+ * 32 and of block_size, at most 64 * block_size); each partition's
+ * attention output o_j, running max m_j and exp-sum l_j go to `workspace`
+ * and a log-sum-exp merge combines them:
+ *   M = max_j m_j,  w_j = l_j * exp(m_j - M),  out = sum_j w_j o_j / sum_j w_j.
+ * A sequence that fits one partition is written directly.  workspace must
+ * hold pa_decode_workspace_bytes(...) bytes (device, 256-byte aligned); its
+ * contents on entry do not matter.  With partition_size == 0 every
+ * sequence is processed in one pass and workspace may be NULL.
+ * ------------------------------------------------------------------------ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq,
+                                 int32_t partition_size);
+
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    int32_t num_kv_heads, float scale, void* out, void* stream,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                    pa_dtype dtype, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator (no device memory, no HIP calls; not thread-safe).
+ * Follows "Paged attention in LLMs" ("The fix", "Keeping track: the block
+ * table", "Sharing blocks") and the MCQ page's copy-on-write row:
+ *  - free pool: a FIFO queue, initially `free_order` (NULL = 0..num_blocks-1);
+ *    freed blocks join its tail, walked from logical block 0 upward;
+ *  - append(seq, n): token at position pos takes slot table[pos/bs]*bs +
+ *    pos%bs; a new block is popped when pos % bs == 0; if the sequence's
+ *    partially filled last block is shared (reference count > 1) the first
+ *    appended token first copies it to a fresh block and records the
+ *    (source, destination) pair, the last holder writes in place;
+ *    all or nothing: PA_ERR_OOM leaves the state unchanged;
+ *  - fork(parent, child): child gets a copy of parent's table and length,
+ *    every block's reference count goes up by one;
+ *  - free(seq): every block's count goes down; blocks reaching 0 are freed.
+ * Sequence ids are arbitrary int64 keys.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_allocator pa_allocator;
+
+/* NULL on a bad argument (num_blocks < 0, block_size <= 0, free_order not a
+ * permutation of 0..num_blocks-1).  Host memory `free_order` is copied. */
+pa_allocator* pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pa_alloc_destroy(pa_allocator* a);
+pa_status pa_alloc_add_seq(pa_allocator* a, int64_t seq);
+/* slots_out: host int64 [n_tokens] (may be NULL when n_tokens == 0);
+ * cow_pairs_out: host int32 [2 * cow_cap] receives (src, dst) pairs,
+ * *n_cow their count (an append copies at most one block, so cow_cap = 1
+ * always suffices). */
+pa_status pa_alloc_append(pa_allocator* a, int64_t seq, int32_t n_tokens, int64_t* slots_out,
+                          int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow);
+pa_status pa_alloc_fork(pa_allocator* a, int64_t parent, int64_t child);
+pa_status pa_alloc_free(pa_allocator* a, int64_t seq);
+/* Copy up to `cap` table entries of seq into host `out`; *n_blocks and
+ * *seq_len receive the full table length and token count. */
+pa_status pa_alloc_table(const pa_allocator* a, int64_t seq, int32_t* out, int32_t cap,
+                         int32_t* n_blocks, int32_t* seq_len);
+/* Dense decode inputs for a batch: host tables_out [n_seqs][width] (entries
+ * past a sequence's blocks are set to `pad`), host seq_lens_out [n_seqs].
+ * PA_ERR_INVALID_ARG if a table is wider than `width`. */
+pa_status pa_alloc_batch_tables(const pa_allocator* a, const int64_t* seqs, int32_t n_seqs,
+                                int32_t* tables_out, int32_t width, int32_t pad,
+                                int32_t* seq_lens_out);
+/* Reference count of a block (-1 if out of range). */
+int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);
+/* Free queue in order, head first: up to `cap` ids into host `out`, *n = its length. */
+pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n);
+int32_t pa_alloc_num_free(const pa_allocator* a);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

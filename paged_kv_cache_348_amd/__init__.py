@@ -1,0 +1,252 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+A thin Python binding over libpa.so (include/pa.h): argument marshalling
+only.  Every step of the decode path (cache append, block copy, decode
+attention, log-sum-exp merge) runs in the library's HIP kernels; the block
+allocator runs in the library's host C++.  PyTorch supplies device memory
+and streams.
+
+Device cache layout (per layer), X = 16 bytes / element size:
+    k_cache [num_blocks, num_kv_heads, head_dim // X, block_size, X]
+    v_cache [num_blocks, num_kv_heads, head_dim, block_size]
+``logical_view`` presents both as [num_blocks, num_kv_heads, block_size,
+head_dim], the pages' per-layer layout.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from ._lib import (PA_BF16, PA_ERR_EXISTS, PA_ERR_INVALID_ARG, PA_ERR_LAUNCH, PA_ERR_NOT_FOUND, PA_ERR_OOM,
+                   PA_ERR_UNSUPPORTED, PA_F32, PA_OK, P_I32, P_I64, PAError, check, lib, status_string)
+
+__all__ = [
+    "PAError", "Allocator", "cache_write", "copy_blocks", "decode", "decode_workspace_bytes", "new_kv_cache",
+    "kv_cache_shapes", "logical_view", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_OOM",
+    "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "status_string", "lib",
+]
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return PA_BF16
+    if dtype == torch.float32:
+        return PA_F32
+    raise TypeError(f"unsupported dtype {dtype} (bfloat16 or float32)")
+
+
+def _elem_bytes(dtype) -> int:
+    return 2 if _dtype_code(dtype) == PA_BF16 else 4
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def kv_cache_shapes(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                    dtype) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
+    x = 16 // _elem_bytes(dtype)
+    if head_dim % x:
+        raise ValueError("head_dim must be a multiple of 16 bytes of elements")
+    return ((num_blocks, num_kv_heads, head_dim // x, block_size, x), (num_blocks, num_kv_heads, head_dim, block_size))
+
+
+def new_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, dtype=None,
+                 device="cuda", nan_fill: bool = False):
+    """Allocate one layer's (k_cache, v_cache).  ``nan_fill`` poisons every slot with NaN."""
+    torch = _torch()
+    dtype = torch.bfloat16 if dtype is None else dtype
+    ks, vs = kv_cache_shapes(num_blocks, num_kv_heads, block_size, head_dim, dtype)
+    if nan_fill:
+        k = torch.full(ks, float("nan"), dtype=dtype, device=device)
+        v = torch.full(vs, float("nan"), dtype=dtype, device=device)
+    else:
+        k = torch.empty(ks, dtype=dtype, device=device)
+        v = torch.empty(vs, dtype=dtype, device=device)
+    return k, v
+
+
+def _pool_dims(k_cache, v_cache):
+    if k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be [NB, Hkv, D/X, bs, X] and v_cache [NB, Hkv, D, bs]")
+    nb, hkv, dx, bs, x = k_cache.shape
+    d = dx * x
+    if tuple(v_cache.shape) != (nb, hkv, d, bs) or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache disagree")
+    if x * _elem_bytes(k_cache.dtype) != 16:
+        raise ValueError("innermost key axis must span 16 bytes")
+    return nb, hkv, bs, d
+
+
+def logical_view(k_cache, v_cache):
+    """Both caches as [NB, Hkv, bs, D] (the keys are gathered into a new tensor, the values are a view)."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    return k_cache.permute(0, 1, 3, 2, 4).reshape(nb, hkv, bs, d), v_cache.transpose(2, 3)
+
+
+def cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Write token t's K/V ([T, Hkv, D] each) into slot slot_mapping[t] (int64; < 0 skips)."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    T = k.shape[0] if k.dim() == 3 else 0
+    if k.shape != v.shape or (T and tuple(k.shape[1:]) != (hkv, d)):
+        raise ValueError("k and v must be [T, num_kv_heads, head_dim]")
+    if slot_mapping.dtype != _torch().int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [T]")
+    if k.dtype != k_cache.dtype:
+        raise ValueError("k/v and cache dtypes differ")
+    if T == 0:
+        return
+    check(lib().pa_cache_write(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"),
+                               _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), T, hkv, d, bs, nb,
+                               _dtype_code(k.dtype), _stream_ptr(stream)), "pa_cache_write")
+
+
+def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """Copy whole blocks: pairs is int32 [n, 2] of (source, destination)."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    if pairs.dtype != _torch().int32 or (pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2)):
+        raise ValueError("pairs must be int32 [n, 2]")
+    n = pairs.shape[0] if pairs.numel() else 0
+    if n == 0:
+        return
+    check(lib().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(pairs, "pairs"), n, hkv, d,
+                               bs, nb, _dtype_code(k_cache.dtype), _stream_ptr(stream)), "pa_copy_blocks")
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, block_size: int,
+                           max_blocks_per_seq: int, partition_size: int) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq,
+                                               partition_size))
+
+
+def decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale: float, out=None,
+           partition_size: int = 0, workspace=None, stream=None):
+    """Decode attention; returns ``out`` [B, Hq, D] (q's dtype)."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    if hkv != num_kv_heads:
+        raise ValueError("num_kv_heads does not match the cache")
+    B, hq, dq = q.shape
+    if dq != d or q.dtype != k_cache.dtype:
+        raise ValueError("q must be [B, Hq, head_dim] in the cache dtype")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("seq_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    mb = block_tables.shape[1]
+    need = decode_workspace_bytes(B, hq, d, bs, mb, partition_size) if B else 0
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    check(lib().pa_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                          _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), hkv, float(scale),
+                          _dev(out, "out"), _stream_ptr(stream), B, hq, d, bs, nb, mb, _dtype_code(q.dtype),
+                          partition_size, ws_ptr, ws_bytes), "pa_decode")
+    return out
+
+
+class Allocator:
+    """Host block allocator (libpa's pa_alloc_*): on-demand blocks, fork, copy-on-write, free."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        self._lib = lib()
+        self.num_blocks, self.block_size = num_blocks, block_size
+        if free_order is not None:
+            fo = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if fo.shape != (num_blocks,):
+                raise ValueError("free_order must list every block once")
+            ptr = fo.ctypes.data_as(P_I32)
+        else:
+            ptr = None
+        self._h = self._lib.pa_alloc_create(num_blocks, block_size, ptr)
+        if not self._h:
+            raise ValueError("pa_alloc_create rejected its arguments")
+        self._slots = np.zeros(1, dtype=np.int64)
+        self._cow = np.zeros(2, dtype=np.int32)
+        self._ncow = ctypes.c_int32(0)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.pa_alloc_destroy(h)
+            self._h = None
+
+    def add_seq(self, seq: int) -> None:
+        check(self._lib.pa_alloc_add_seq(self._h, seq), "pa_alloc_add_seq")
+
+    def append(self, seq: int, n: int):
+        """Returns (slots int64 [n], copy pairs [(src, dst)])."""
+        if self._slots.shape[0] < max(n, 1):
+            self._slots = np.zeros(max(n, 2 * self._slots.shape[0]), dtype=np.int64)
+        st = self._lib.pa_alloc_append(self._h, seq, n, self._slots.ctypes.data_as(P_I64),
+                                       self._cow.ctypes.data_as(P_I32), 1, ctypes.byref(self._ncow))
+        check(st, "pa_alloc_append")
+        pairs = [(int(self._cow[0]), int(self._cow[1]))] if self._ncow.value else []
+        return self._slots[:n].copy(), pairs
+
+    def fork(self, parent: int, child: int) -> None:
+        check(self._lib.pa_alloc_fork(self._h, parent, child), "pa_alloc_fork")
+
+    def free(self, seq: int) -> None:
+        check(self._lib.pa_alloc_free(self._h, seq), "pa_alloc_free")
+
+    def table(self, seq: int):
+        """(table as a list, length in tokens)."""
+        nbk, ln = ctypes.c_int32(0), ctypes.c_int32(0)
+        check(self._lib.pa_alloc_table(self._h, seq, None, 0, ctypes.byref(nbk), ctypes.byref(ln)), "pa_alloc_table")
+        out = np.zeros(max(nbk.value, 1), dtype=np.int32)
+        check(self._lib.pa_alloc_table(self._h, seq, out.ctypes.data_as(P_I32), nbk.value, ctypes.byref(nbk),
+                                       ctypes.byref(ln)), "pa_alloc_table")
+        return out[:nbk.value].tolist(), ln.value
+
+    def batch_tables(self, seqs: Sequence[int], width: Optional[int] = None, pad: int = 0):
+        """Dense (block_tables int32 [B, width], seq_lens int32 [B]) for a decode call."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        if width is None:
+            width = max([len(self.table(int(s))[0]) for s in seqs] + [1])
+        tables = np.zeros((len(seqs), width), dtype=np.int32)
+        lens = np.zeros(len(seqs), dtype=np.int32)
+        check(self._lib.pa_alloc_batch_tables(self._h, seqs.ctypes.data_as(P_I64), len(seqs),
+                                              tables.ctypes.data_as(P_I32), width, pad, lens.ctypes.data_as(P_I32)),
+              "pa_alloc_batch_tables")
+        return tables, lens
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_alloc_refcount(self._h, block))
+
+    def free_list(self):
+        n = ctypes.c_int32(0)
+        check(self._lib.pa_alloc_free_list(self._h, None, 0, ctypes.byref(n)), "pa_alloc_free_list")
+        out = np.zeros(max(n.value, 1), dtype=np.int32)
+        check(self._lib.pa_alloc_free_list(self._h, out.ctypes.data_as(P_I32), n.value, ctypes.byref(n)),
+              "pa_alloc_free_list")
+        return out[:n.value].tolist()
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_alloc_num_free(self._h))

@@ -1,0 +1,79 @@
+"""Build libpa.so (the C-ABI library) in-tree for gfx950 with hipcc.
+
+    python -m paged_kv_cache_348_amd.build [--asm]
+
+Compiles every source under csrc/ into paged_kv_cache_348_amd/libpa.so.
+``--asm`` also writes the device assembly of each HIP source under _build/.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libpa.so")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Packed-FP32 instructions are kept out of the device code on purpose.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]
+
+
+def sources():
+    hip = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    cpp = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".cpp"))
+    return hip, cpp
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(line for line in r.stdout.splitlines() if "packed-fp32-ops" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(asm: bool = False, verbose: bool = False) -> str:
+    hip, cpp = sources()
+    tmp = tempfile.mkdtemp(prefix="pa_build_")
+    try:
+        jobs = []
+        objs = []
+        for src in hip:
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            objs.append(obj)
+            jobs.append([HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj])
+        for src in cpp:
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            objs.append(obj)
+            jobs.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-c", src, "-o", obj])
+        if asm:
+            os.makedirs(os.path.join(ROOT, "_build"), exist_ok=True)
+            for src in hip:
+                out = os.path.join(ROOT, "_build", os.path.basename(src) + ".s")
+                jobs.append([HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "--cuda-device-only",
+                             "-S", src, "-o", out])
+        with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+            for out in ex.map(_run, jobs):
+                if verbose and out.strip():
+                    print(out)
+        tmp_lib = os.path.join(tmp, "libpa.so")
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib])
+        shutil.move(tmp_lib, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    path = build(asm="--asm" in sys.argv, verbose=True)
+    print(path)

@@ -1,0 +1,130 @@
+// Cache append (pa_cache_write) and whole-block copy (pa_copy_blocks).
+//
+// The cache grows by one token's keys and values per step, and each token
+// lands in the slot its request's block table gives it ("Paged attention in
+// LLMs", "The cache being stored"; PagedAttention MCQ page, code sketch).
+// A shared block is copied whole before a request writes into it (MCQ page,
+// comparison table, "Copy on write blocks").
+//
+// Pool tile layout (include/pa.h): keys [head_dim/X][block_size][X], values
+// [head_dim][block_size] per (block, kv-head), X = 16 bytes of elements.
+// One thread moves one 16-byte chunk of a token's key (a 16-byte store) and
+// the same chunk of its value (X element stores, block_size apart).
+
+#include <cstdint>
+
+#include "pa.h"
+#include "pa_device.h"
+
+namespace pa {
+
+template <int ES>
+__global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict__ k, const char* __restrict__ v,
+                                                          const int64_t* __restrict__ slots, char* __restrict__ kc,
+                                                          char* __restrict__ vc, int64_t n_chunks, int Hkv, int D,
+                                                          int BS, int64_t total_slots) {
+    constexpr int X = 16 / ES;
+    const int C = D / X;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_chunks) return;
+    const int c = (int)(idx % C);
+    const int64_t th = idx / C;  // token * Hkv + head
+    const int h = (int)(th % Hkv);
+    const int64_t t = th / Hkv;
+    const int64_t s = slots[t];
+    if (s < 0 || s >= total_slots) return;
+    const int64_t blk = s / BS;
+    const int off = (int)(s % BS);
+    const int64_t tile = (blk * Hkv + h) * (int64_t)D * BS;  // element offset of the (block, head) tile
+    const int64_t src = (th * D + (int64_t)c * X) * ES;
+    st16(kc + (tile + ((int64_t)c * BS + off) * X) * ES, ld16(k + src));
+    const u32x4 vv = ld16(v + src);
+    if constexpr (ES == 2) {
+        uint16_t* vt = reinterpret_cast<uint16_t*>(vc) + tile + (int64_t)c * X * BS + off;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vt[(int64_t)e * BS] = (uint16_t)(vv[e >> 1] >> (16 * (e & 1)));
+    } else {
+        uint32_t* vt = reinterpret_cast<uint32_t*>(vc) + tile + (int64_t)c * X * BS + off;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vt[(int64_t)e * BS] = vv[e];
+    }
+}
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc,
+                                                          const int32_t* __restrict__ pairs, int64_t block_bytes,
+                                                          int num_blocks) {
+    const int pi = blockIdx.y;
+    const int32_t src = pairs[2 * pi];
+    const int32_t dst = pairs[2 * pi + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+    const int64_t nvec = block_bytes / 16;
+    const int64_t so = (int64_t)src * block_bytes, dO = (int64_t)dst * block_bytes;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * blockDim.x) {
+        st16(kc + dO + i * 16, ld16(kc + so + i * 16));
+        st16(vc + dO + i * 16, ld16(vc + so + i * 16));
+    }
+}
+
+}  // namespace pa
+
+namespace {
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline pa_status check_pool(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            pa_dtype dtype) {
+    if (num_kv_heads <= 0 || num_blocks < 0) return PA_ERR_INVALID_ARG;
+    if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != 8 && block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+}  // namespace
+
+extern "C" pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                                    void* v_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
+    if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+    pa_status st = check_pool(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+    if (st != PA_OK) return st;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+    if (!al16(k) || !al16(v) || !al16(k_cache) || !al16(v_cache) || (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+        return PA_ERR_INVALID_ARG;
+    const int es = dtype == PA_BF16 ? 2 : 4;
+    const int64_t chunks = (int64_t)num_tokens * num_kv_heads * (head_dim * es / 16);
+    const int64_t grid = (chunks + 255) / 256;
+    if (grid > 2147483647LL) return PA_ERR_UNSUPPORTED;
+    const int64_t total_slots = (int64_t)num_blocks * block_size;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (dtype == PA_BF16)
+        hipLaunchKernelGGL((pa::cache_write_kernel<2>), dim3((unsigned)grid), dim3(256), 0, s,
+                           reinterpret_cast<const char*>(k), reinterpret_cast<const char*>(v), slot_mapping,
+                           reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache), chunks, num_kv_heads,
+                           head_dim, block_size, total_slots);
+    else
+        hipLaunchKernelGGL((pa::cache_write_kernel<4>), dim3((unsigned)grid), dim3(256), 0, s,
+                           reinterpret_cast<const char*>(k), reinterpret_cast<const char*>(v), slot_mapping,
+                           reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache), chunks, num_kv_heads,
+                           head_dim, block_size, total_slots);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    pa_dtype dtype, void* stream) {
+    if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+    pa_status st = check_pool(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+    if (st != PA_OK) return st;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !pairs) return PA_ERR_INVALID_ARG;
+    if (!al16(k_cache) || !al16(v_cache) || (reinterpret_cast<uintptr_t>(pairs) & 3u)) return PA_ERR_INVALID_ARG;
+    if (num_pairs > 65535) return PA_ERR_UNSUPPORTED;
+    const int es = dtype == PA_BF16 ? 2 : 4;
+    const int64_t block_bytes = (int64_t)num_kv_heads * head_dim * block_size * es;
+    int64_t gx = (block_bytes / 16 + 255) / 256;
+    if (gx > 64) gx = 64;
+    hipLaunchKernelGGL(pa::copy_blocks_kernel, dim3((unsigned)gx, (unsigned)num_pairs), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<char*>(k_cache),
+                       reinterpret_cast<char*>(v_cache), pairs, block_bytes, num_blocks);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}

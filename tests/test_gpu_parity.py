@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+* cache bytes: after the replay and the decode-step append, the whole
+  device pool (read in the pages' [block, head, slot, dim] order) equals
+  the oracle's pool bit for bit, NaN poison of unwritten slots included;
+* decode output: within 1e-5 (float32 cache) or 2e-2 (bfloat16 cache,
+  float32 accumulation) of the float64 oracle, with no NaN;
+* split (partitioned + log-sum-exp merge) and single-pass both;
+* bitwise invariances the design guarantees: the result does not depend on
+  which physical blocks hold the tokens, nor on which other sequences
+  share the batch;
+* edge cases: empty and one-token sequences, lengths at and around block
+  and step boundaries, group sizes 1..16, head dim 64 and 128, every block
+  size, invalid table entries and over-long lengths (NaN rows, no fault).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_348_amd as pa  # noqa: E402
+from paged_kv_cache_348_amd.workload import build_device_batch  # noqa: E402
+import oracle.attention as oa  # noqa: E402
+from oracle.cache import replay  # noqa: E402
+from synthetic import make_workload  # noqa: E402
+from synthetic.workloads import custom  # noqa: E402
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def host_bits(t):
+    t = t.contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.view(torch.int32).numpy().view(np.uint32)
+
+
+def out_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_out(got, ref, dtype, rows=None, what=""):
+    rows = range(got.shape[0]) if rows is None else rows
+    g = got[list(rows)]
+    r = ref[list(rows)]
+    assert not np.isnan(g).any(), f"{what}: NaN in output"
+    err = np.abs(g - r)
+    worst = np.unravel_index(np.argmax(err), err.shape) if err.size else None
+    say(f"{what}: max abs err {err.max() if err.size else 0:.3e} at {worst}")
+    assert err.max() <= TOL[dtype], f"{what}: max abs err {err.max()} at {worst}"
+
+
+def oracle_for(w):
+    pool, _, tables, dslots, _ = replay(w)
+    out = oa.paged_decode(w.q, pool.k, pool.v, tables, w.seq_lens, w.scale)
+    return pool, out
+
+
+SMALL = [
+    ("tiny", "tiny", {}),
+    ("llama3_8b_small", "llama3_8b", dict(batch=6, len_lo=1, len_hi=700)),
+    ("llama_70b_small", "llama_70b", dict(batch=6, len_lo=40, len_hi=600)),
+    ("prefix_share_small", "prefix_share", dict(prompts=2, samples=8, prompt_len=2040, tail_max=70)),
+    ("long_ctx_bs8_small", "long_ctx_bs8", dict(batch=3, len_lo=1500, len_hi=3000)),
+    ("long_ctx_bs16_small", "long_ctx_bs16", dict(batch=3, len_lo=1500, len_hi=3000)),
+    ("long_ctx_bs32_small", "long_ctx_bs32", dict(batch=3, len_lo=1500, len_hi=3000)),
+]
+
+
+@pytest.mark.parametrize("label,name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_cache_and_decode_match_oracle(label, name, kw):
+    w = make_workload(name, seed=0, **kw)
+    say(label, "B", w.batch, "max L", w.max_seq_len, "NB", w.num_blocks)
+    pool, ref = oracle_for(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    torch.cuda.synchronize()
+    kl, vl = pa.logical_view(dev.k_cache, dev.v_cache)
+    kb, vb = pool.bits()
+    assert np.array_equal(host_bits(kl), kb), "key pool differs"
+    assert np.array_equal(host_bits(vl), vb), "value pool differs"
+    for ps in sorted({0, w.partition_size, 32, 64, 512}):
+        say(label, "partition", ps)
+        out = dev.attend(partition_size=ps)
+        torch.cuda.synchronize()
+        check_out(out_f64(out), ref, w.dtype, what=f"{label} ps={ps}")
+
+
+EDGE = [
+    # (dtype, Hq, Hkv, D, bs, lens)
+    ("bf16", 32, 8, 128, 16, [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65]),
+    ("bf16", 8, 8, 128, 8, [0, 1, 7, 8, 9, 40, 97]),
+    ("bf16", 16, 1, 128, 32, [1, 33, 100, 257]),
+    ("bf16", 64, 8, 64, 16, [5, 128, 300]),
+    ("bf16", 12, 4, 64, 32, [0, 31, 32, 200]),
+    ("bf16", 2, 2, 128, 8, [513, 1025]),
+    ("f32", 8, 8, 64, 16, [14, 60, 1, 33]),
+    ("f32", 32, 8, 128, 8, [1, 9, 16, 17, 160]),
+    ("f32", 16, 1, 64, 32, [0, 3, 64, 99]),
+    ("f32", 6, 2, 128, 16, [700]),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: f"{c[0]}-Hq{c[1]}-Hkv{c[2]}-D{c[3]}-bs{c[4]}")
+def test_edge_shapes(case):
+    dtype, hq, hkv, d, bs, lens = case
+    w = custom(seed=sum(lens) + d + bs + hq, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+               lens=lens)
+    say("edge", case)
+    pool, ref = oracle_for(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    for ps in (0, 32, 64):
+        out = out_f64(dev.attend(partition_size=ps))
+        torch.cuda.synchronize()
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.array_equal(out[b], np.zeros_like(out[b])), "empty sequence must give zeros"
+        check_out(out, ref, dtype, what=f"edge {case} ps={ps}")
+        # one key: the output is that key's value, up to the output rounding
+        for b, L in enumerate(lens):
+            if L == 1:
+                np.testing.assert_array_equal(out[b], ref[b])
+
+
+def test_block_placement_is_bitwise_invisible():
+    base = dict(dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                lens=[1, 77, 300, 1024, 2047])
+    outs = []
+    for order in ("seeded", "identity", "reversed"):
+        w = custom(seed=5, **base)
+        if order == "identity":
+            w.free_order = np.arange(w.num_blocks, dtype=np.int32)
+        elif order == "reversed":
+            w.free_order = w.free_order[::-1].copy()
+        dev = build_device_batch(w)
+        dev.cache_append()
+        for ps in (0, 512):
+            outs.append((order, ps, host_bits(dev.attend(partition_size=ps))))
+    torch.cuda.synchronize()
+    for ps in (0, 512):
+        ref = [o for o in outs if o[1] == ps]
+        for o in ref[1:]:
+            assert np.array_equal(o[2], ref[0][2]), f"placement {o[0]} changed the result (ps={ps})"
+
+
+def test_batch_neighbours_do_not_change_a_row():
+    w = custom(seed=6, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+               lens=[900, 3, 2500, 64])
+    dev = build_device_batch(w)
+    dev.cache_append()
+    full = host_bits(dev.attend(partition_size=512))
+    for b in range(w.batch):
+        sub = pa.decode(dev.q[b:b + 1].contiguous(), dev.k_cache, dev.v_cache, dev.block_tables[b:b + 1].contiguous(),
+                        dev.seq_lens[b:b + 1].contiguous(), w.num_kv_heads, w.scale, partition_size=512)
+        assert np.array_equal(host_bits(sub)[0], full[b])
+
+
+def test_invalid_device_data_gives_nan_rows_without_fault():
+    w = custom(seed=7, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, lens=[40, 50, 60])
+    dev = build_device_batch(w)
+    dev.cache_append()
+    tables = dev.block_tables.clone()
+    tables[1, 2] = w.num_blocks + 5  # entry 2 is read (50 tokens need 4 blocks)
+    tables[2, 0] = -1
+    lens = dev.seq_lens.clone()
+    lens[0] = tables.shape[1] * 16 + 1  # longer than its table row
+    for ps in (0, 32):
+        out = pa.decode(dev.q, dev.k_cache, dev.v_cache, tables, lens, w.num_kv_heads, w.scale, partition_size=ps)
+        o = out_f64(out)
+        assert np.isnan(o).all(), "every row of this batch is invalid"
+    # a valid table again gives finite output: nothing was corrupted
+    out = out_f64(dev.attend(partition_size=32))
+    assert np.isfinite(out).all()
+
+
+def test_out_of_pool_slots_are_skipped():
+    w = custom(seed=8, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=8, lens=[10, 20])
+    dev = build_device_batch(w)
+    before_k, before_v = (host_bits(x) for x in pa.logical_view(dev.k_cache, dev.v_cache))
+    bad = torch.tensor([w.num_blocks * 8, -1], dtype=torch.int64, device="cuda")
+    pa.cache_write(dev.dec_k, dev.dec_v, bad, dev.k_cache, dev.v_cache)
+    torch.cuda.synchronize()
+    after_k, after_v = (host_bits(x) for x in pa.logical_view(dev.k_cache, dev.v_cache))
+    assert np.array_equal(before_k, after_k) and np.array_equal(before_v, after_v)
