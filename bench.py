@@ -1,0 +1,292 @@
+"""Decode-step benchmark on one MI355X: paged single-query decode attention.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b]
+                    [--partition-size P] [--no-cpu]
+
+One step is one pass of the whole hot path over one batch: the cache append
+of every sequence's decode token (pa_cache_write) followed by the decode
+attention (pa_decode, with its split-sequence merge when partitioned).  The
+inputs (pool, block tables, queries, decode tokens) are resident in HBM
+before the timed region starts.  The default workload is the
+Llama-3-8B-shaped decode layer: 64 sequences, 32 query / 8 KV heads, head
+dim 128, block size 16, bfloat16, lengths uniform in [512, 4096], blocks
+placed by a seeded random permutation of a pool sized to demand + 10 %.
+
+Printed: one JSON line with decode tokens/s (``value``), the KV-read
+bandwidth, a roofline entry for the decode kernel (algorithmic KV bytes per
+launch / its average duration, timed with HIP events on the launch stream)
+and the CPU oracle timed on this host's cores on the same workload
+(``cpu_baseline``; it runs before the GPU is touched).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from synthetic import make_workload  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_PARTITION = {"llama3_8b": 512, "llama_70b": 512, "prefix_share": 512}
+WORKLOAD_TEXT = {
+    "llama3_8b": "Llama-3-8B-shaped decode layer: batch 64, 32 q / 8 kv heads (GQA 4), d_head 128, block 16, "
+                 "bf16, seq_lens U[512,4096], seeded random block permutation of a pool = demand + 10%",
+    "llama_70b": "70B-shaped decode layer: batch 256, 64 q / 8 kv heads (GQA 8), d_head 128, block 16, bf16, "
+                 "seq_lens U[1024,8192], pool fragmented by an interleaved arrival/finish trace",
+    "prefix_share": "parallel sampling: 32 prompts x 8 samples, shared 2040-token prompt, tails U[0,512], "
+                    "copy-on-write of the partial prompt block, 32 q / 8 kv heads, d_head 128, bf16",
+    "long_ctx_bs8": "long-context split decode: batch 8, seq_lens U[32768,131072], 32 q / 8 kv heads, d_head 128, "
+                    "bf16, block 8, 512-token partitions + log-sum-exp merge",
+    "long_ctx_bs16": "long-context split decode: batch 8, seq_lens U[32768,131072], 32 q / 8 kv heads, d_head 128, "
+                     "bf16, block 16, 512-token partitions + log-sum-exp merge",
+    "long_ctx_bs32": "long-context split decode: batch 8, seq_lens U[32768,131072], 32 q / 8 kv heads, d_head 128, "
+                     "bf16, block 32, 512-token partitions + log-sum-exp merge",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------- CPU baseline (the oracle)
+
+_CPU = {}
+
+
+def _cpu_init():
+    try:
+        from threadpoolctl import threadpool_limits
+
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _cpu_one(b):
+    import oracle.attention as oa
+
+    c = _CPU
+    L = int(c["lens"][b])
+    if L <= 0:
+        return b, np.zeros(c["q"].shape[1:])
+    K, V = oa.gather_sequence(c["k"], c["v"], c["tables"][b], L)
+    return b, oa.dense_attention(oa.widen(c["q"][b]), K, V, c["scale"])
+
+
+def cpu_baseline(w, min_seconds: float = 10.0, max_passes: int = 10000):
+    """Time the oracle over the workload's sequences on this host's cores.
+
+    The pool is built by the oracle's own replay (untimed); the timed part
+    is the block-table walk and float64 attention of every sequence, one
+    sequence per task in a process pool.  Whole passes over the batch
+    repeat until ``min_seconds`` of wall time have gone by.
+    """
+    import multiprocessing as mp
+
+    from oracle.cache import replay
+
+    t0 = time.perf_counter()
+    pool, _, tables, _, _ = replay(w)
+    log(f"oracle replay {time.perf_counter() - t0:.1f}s")
+    _CPU.update(k=pool.k, v=pool.v, tables=tables, lens=w.seq_lens, q=w.q, scale=w.scale)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("fork")
+    out = np.zeros((w.batch, w.num_q_heads, w.head_dim))
+    order = sorted(range(w.batch), key=lambda b: -int(w.seq_lens[b]))  # longest first
+    with ctx.Pool(cores, initializer=_cpu_init) as p:
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            for b, o in p.imap_unordered(_cpu_one, order):
+                out[b] = o
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or passes >= max_passes:
+                break
+    tok = passes * w.batch
+    res = {
+        "value": tok / el,
+        "unit": "decode tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"the whole batch ({w.batch} sequences, sum L = {int(w.seq_lens.sum())}) x {passes} passes, "
+                  f"{el:.1f} s; float64 numpy, one sequence per task in a {cores}-process pool",
+        "kv_read_gbps": passes * w.kv_read_bytes() / el / 1e9,
+    }
+    _CPU.clear()
+    return res, out
+
+
+# ---------------------------------------------------------------------------- GPU
+
+
+def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int = 20):
+    import torch
+
+    from paged_kv_cache_348_amd.workload import build_device_batch
+
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"device {dev_name}")
+    t0 = time.perf_counter()
+    dev = build_device_batch(w, device="cuda", partition_size=partition_size)
+    torch.cuda.synchronize()
+    log(f"device pool built in {time.perf_counter() - t0:.1f}s, NB {w.num_blocks}, width {dev.max_blocks}")
+    w.drop_kv()
+    stream = torch.cuda.current_stream()
+
+    for _ in range(warmup):
+        dev.step()
+    torch.cuda.synchronize()
+
+    # timed region: `steps` whole steps (cache append + decode)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        dev.step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = ev0.elapsed_time(ev1) / steps
+    out = dev.out.float().cpu().numpy().astype(np.float64)
+
+    # decode kernel alone: one event pair per launch, hot and with L2/MALL flushed
+    # (the flush reads 1 GiB, so it leaves no dirty lines to write back later)
+    def time_decode(n, flush):
+        scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda") if flush else None
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            if flush:
+                scratch.amax()
+            a.record(stream)
+            dev.attend()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs])
+        del scratch
+        return t
+
+    hot = time_decode(max(steps, 20), False)
+    cold = time_decode(cold_iters, True)
+
+    # cache append alone
+    ca0, ca1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca0.record(stream)
+    for _ in range(steps):
+        dev.cache_append()
+    ca1.record(stream)
+    torch.cuda.synchronize()
+    ms_append = ca0.elapsed_time(ca1) / steps
+    return dict(ms_step=ms_step, wall_s=t_wall, hot_ms=hot, cold_ms=cold, ms_append=ms_append, out=out,
+                device=dev_name, width=dev.max_blocks, launches=dev.launches)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "the decode shards by sequence or KV head with no exchange, see the design notes", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is a single-process, single-GPU benchmark", file=sys.stderr)
+        return 2
+
+    w = make_workload(args.workload, seed=args.seed)
+    ps = args.partition_size
+    if ps is None:
+        ps = w.partition_size or DEFAULT_PARTITION.get(args.workload, 0)
+    kv_bytes = w.kv_read_bytes()
+    log(f"workload {w.name}: B {w.batch}, sum L {int(w.seq_lens.sum())}, KV bytes {kv_bytes / 1e9:.3f} GB, "
+        f"partition {ps}")
+
+    cpu, ref = (None, None)
+    if not args.no_cpu:
+        cpu, ref = cpu_baseline(w, min_seconds=args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.1f} tok/s on {cpu['cores']} cores")
+
+    g = gpu_bench(w, args.steps, args.warmup, ps)
+    ms = g["ms_step"]
+    hot, cold = g["hot_ms"], g["cold_ms"]
+    t_dec = float(hot.mean()) * 1e-3
+    achieved = kv_bytes / t_dec / 1e9
+    err = None
+    if ref is not None:
+        err = float(np.abs(g["out"] - ref).max())
+        log(f"full-size parity vs oracle: max abs err {err:.3e}")
+    flop = 4.0 * w.head_dim * w.num_q_heads * float(w.seq_lens.sum())
+    res = {
+        "metric": "decode attention tokens/s and KV-read HBM GB/s (% of 8 TB/s) on 1 MI355X",
+        "value": w.batch / (ms * 1e-3),
+        "unit": "decode tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v rounded to bf16; seeded lengths and block placement)",
+        "config": {
+            "workload": WORKLOAD_TEXT[args.workload],
+            "name": w.name,
+            "seed": args.seed,
+            "batch": w.batch,
+            "sum_seq_len": int(w.seq_lens.sum()),
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "num_blocks": w.num_blocks,
+            "partition_size": ps,
+            "step": "pa_cache_write (decode tokens) + pa_decode",
+        },
+        "kv_read_gbps_step": kv_bytes / (ms * 1e-3) / 1e9,
+        "kv_read_frac_of_8tbs_step": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "decode_us": {"hot_mean": float(hot.mean()) * 1e3, "hot_min": float(hot.min()) * 1e3,
+                      "cold_median": float(np.median(cold)) * 1e3, "cold_min": float(cold.min()) * 1e3},
+        "cache_append_us": g["ms_append"] * 1e3,
+        "kv_tokens_per_s": float(w.seq_lens.sum()) / t_dec,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "flop_per_launch": flop,
+        },
+        "cpu_baseline": cpu,
+        "max_abs_err_vs_oracle": err,
+        "device": g["device"],
+    }
+    if cpu is not None:
+        cpu.pop("kv_read_gbps", None)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -147,8 +147,8 @@ __global__ __launch_bounds__(64) void decode_kernel(
     float* __restrict__ part_o, float* __restrict__ part_ml, int Hq, int Hkv, int G, int max_blocks,
     int num_blocks, int PS, int P_max, float scale_log2) {
     using C = DecodeCfg<BF16, D, BS>;
-    const int p = blockIdx.x;
-    const int g = blockIdx.y;
+    const int g = blockIdx.x;  // kv-head fastest: consecutive workgroups land on different XCDs
+    const int p = blockIdx.y;
     const int b = blockIdx.z;
     const int lane = threadIdx.x;
     const int n = lane & 15;  // head column: query head g*G + n when n < G
@@ -435,7 +435,7 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, const in
                          const int32_t* lens, void* out, float* po, float* pml, int B, int Hq, int Hkv,
                          int max_blocks, int num_blocks, int PS, int P_max, float scale_log2,
                          hipStream_t stream) {
-    dim3 grid((unsigned)P_max, (unsigned)Hkv, (unsigned)B);
+    dim3 grid((unsigned)Hkv, (unsigned)P_max, (unsigned)B);
     hipLaunchKernelGGL((pa::decode_kernel<BF16, D, BS>), grid, dim3(64), 0, stream, q, kc, vc, tables, lens, out,
                        po, pml, Hq, Hkv, Hq / Hkv, max_blocks, num_blocks, PS, P_max, scale_log2);
     hipError_t e = hipGetLastError();
@@ -504,7 +504,7 @@ extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v
 
     int64_t ps, pmax;
     partition_plan(block_size, max_blocks_per_seq, partition_size, &ps, &pmax);
-    if (pmax > 2147483647LL) return PA_ERR_UNSUPPORTED;
+    if (pmax > 65535) return PA_ERR_UNSUPPORTED;
     float* po = nullptr;
     float* pml = nullptr;
     if (pmax > 1) {
