@@ -179,6 +179,25 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
     hot = time_decode(max(steps, 20), False)
     cold = time_decode(cold_iters, True)
 
+    # calibration: a plain streaming read of the same byte count
+    import paged_kv_cache_348_amd as pa
+
+    nbytes = (w.kv_read_bytes() + 4095) // 4096 * 4096
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pa.stream_read(buf, sink)
+    sr = []
+    for _ in range(max(steps, 20)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        pa.stream_read(buf, sink)
+        b.record(stream)
+        sr.append((a, b))
+    torch.cuda.synchronize()
+    sr_ms = float(np.mean([a.elapsed_time(b) for a, b in sr]))
+    del buf
+
     # cache append alone
     ca0, ca1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ca0.record(stream)
@@ -188,6 +207,7 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
     torch.cuda.synchronize()
     ms_append = ca0.elapsed_time(ca1) / steps
     return dict(ms_step=ms_step, wall_s=t_wall, hot_ms=hot, cold_ms=cold, ms_append=ms_append, out=out,
+                stream_read_gbps=nbytes / (sr_ms * 1e-3) / 1e9,
                 device=dev_name, width=dev.max_blocks, launches=dev.launches)
 
 
@@ -200,6 +220,9 @@ def main(argv=None):
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--block-order", choices=("seeded", "identity"), default="seeded",
+                    help="identity: the free pool starts in address order, so each sequence's blocks are "
+                         "mostly adjacent (the block-table lookup-overhead comparison)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args(argv)
 
@@ -212,6 +235,8 @@ def main(argv=None):
         return 2
 
     w = make_workload(args.workload, seed=args.seed)
+    if args.block_order == "identity":
+        w.free_order = np.arange(w.num_blocks, dtype=np.int32)
     ps = args.partition_size
     if ps is None:
         ps = w.partition_size or DEFAULT_PARTITION.get(args.workload, 0)
@@ -260,12 +285,14 @@ def main(argv=None):
             "num_blocks": w.num_blocks,
             "partition_size": ps,
             "step": "pa_cache_write (decode tokens) + pa_decode",
+            "block_order": args.block_order,
         },
         "kv_read_gbps_step": kv_bytes / (ms * 1e-3) / 1e9,
         "kv_read_frac_of_8tbs_step": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "decode_us": {"hot_mean": float(hot.mean()) * 1e3, "hot_min": float(hot.min()) * 1e3,
                       "cold_median": float(np.median(cold)) * 1e3, "cold_min": float(cold.min()) * 1e3},
         "cache_append_us": g["ms_append"] * 1e3,
+        "stream_read_gbps_same_bytes": g["stream_read_gbps"],
         "kv_tokens_per_s": float(w.seq_lens.sum()) / t_dec,
         "roofline": {
             "bound": "hbm",

@@ -24,7 +24,7 @@ from ._lib import (PA_BF16, PA_ERR_EXISTS, PA_ERR_INVALID_ARG, PA_ERR_LAUNCH, PA
 
 __all__ = [
     "PAError", "Allocator", "cache_write", "copy_blocks", "decode", "decode_workspace_bytes", "new_kv_cache",
-    "kv_cache_shapes", "logical_view", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_OOM",
+    "kv_cache_shapes", "logical_view", "stream_read", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_OOM",
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "status_string", "lib",
 ]
 
@@ -169,6 +169,14 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale
                           _dev(out, "out"), _stream_ptr(stream), B, hq, d, bs, nb, mb, _dtype_code(q.dtype),
                           partition_size, ws_ptr, ws_bytes), "pa_decode")
     return out
+
+
+def stream_read(buf, sink, workgroups: int = 0, stream=None) -> None:
+    """Measurement helper: read every byte of device tensor ``buf`` once (pa_bench_stream_read)."""
+    if sink.dtype != _torch().int32 or sink.numel() < 1:
+        raise ValueError("sink must be a device int32 tensor")
+    check(lib().pa_bench_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"),
+                                     workgroups, _stream_ptr(stream)), "pa_bench_stream_read")
 
 
 class Allocator:

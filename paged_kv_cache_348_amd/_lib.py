@@ -19,7 +19,7 @@ P_I64 = ctypes.POINTER(ctypes.c_int64)
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_NOT_FOUND, PA_ERR_LAUNCH, PA_ERR_EXISTS = range(7)
 PA_F32, PA_BF16 = 0, 1
 
-# (name, restype, argtypes) of every symbol include/pa.h declares
+# (name, restype, argtypes) of every symbol include/pa.h and include/pa_bench.h declare
 SIGNATURES = [
     ("pa_status_string", ctypes.c_char_p, [c_int32]),
     ("pa_cache_write", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
@@ -41,6 +41,8 @@ SIGNATURES = [
     ("pa_alloc_refcount", c_int32, [c_void_p, c_int32]),
     ("pa_alloc_free_list", c_int32, [c_void_p, P_I32, c_int32, P_I32]),
     ("pa_alloc_num_free", c_int32, [c_void_p]),
+    # include/pa_bench.h
+    ("pa_bench_stream_read", c_int32, [c_void_p, c_size_t, c_void_p, c_int32, c_void_p]),
 ]
 
 _lib = None

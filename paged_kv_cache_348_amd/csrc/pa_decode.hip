@@ -112,7 +112,7 @@ __device__ __forceinline__ void issue_step(StepRegs<BF16, D, BS>& r, const char*
 #pragma unroll
         for (int c = 0; c < C::NKC; ++c) {
             const int chunk = 4 * c + j;  // 16-byte chunk of the head dim
-            r.k[t][c] = ld16(kp + (int64_t)chunk * BS * 16);
+            r.k[t][c] = ld16_stream(kp + (int64_t)chunk * BS * 16);
         }
     }
     // values: lane group j reads tokens [tok0 + VT*j, +VT) of head-dim row d
@@ -123,7 +123,7 @@ __device__ __forceinline__ void issue_step(StepRegs<BF16, D, BS>& r, const char*
 #pragma unroll
     for (int c = 0; c < C::NV; ++c) {
         const int d = 16 * c + n;
-        r.v[c] = ld16(vp + (int64_t)d * BS * C::ES);
+        r.v[c] = ld16_stream(vp + (int64_t)d * BS * C::ES);
     }
 }
 
@@ -139,6 +139,119 @@ __device__ __forceinline__ float wave_sum16(float x) {
     x += shfl_xor_f(x, 32);
     return x;
 }
+
+// One loop step: scores of the step's tokens for the G query heads, the
+// online-softmax update and the PV accumulation.  Tokens at or past L are
+// masked: their scores become -inf and their values are zeroed, since a
+// stale or NaN value times a zero weight would still poison the sum.
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
+                                             const u32x4 (&qr)[DecodeCfg<BF16, D, BS>::NKC], float& m_run,
+                                             float& l_run, f32x4 (&acc)[DecodeCfg<BF16, D, BS>::NV], int tok0,
+                                             int L, int j, float scale_log2) {
+    using C = DecodeCfg<BF16, D, BS>;
+    const bool tail = tok0 + C::STEP > L;
+    if constexpr (BF16) {
+        // ---- scores: two 16-token tiles, rows 4j+i <-> tokens 8j+i (tile a), 8j+4+i (tile b)
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < C::NKC; ++c) {
+            const bf16x8 qv = __builtin_bit_cast(bf16x8, qr[c]);
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[0][c]), qv, sa,
+                                                        0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[1][c]), qv, sb,
+                                                        0, 0, 0);
+        }
+        float s[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[i] = sa[i] * scale_log2;
+            s[4 + i] = sb[i] * scale_log2;
+        }
+        if (tail) {
+            const int base = tok0 + 8 * j;
+            uint32_t keep[4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] = (base + e < L) ? s[e] : -INFINITY;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                keep[w] = ((base + 2 * w < L) ? 0x0000ffffu : 0u) | ((base + 2 * w + 1 < L) ? 0xffff0000u : 0u);
+            // values of masked tokens may be NaN: zero them (p = 0 would not)
+#pragma unroll
+            for (int c = 0; c < C::NV; ++c)
+                cur.v[c] = u32x4{cur.v[c][0] & keep[0], cur.v[c][1] & keep[1], cur.v[c][2] & keep[2],
+                                 cur.v[c][3] & keep[3]};
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+        mx = wave_max16(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float pe[8];
+        float rs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pe[e] = __builtin_amdgcn_exp2f(s[e] - m_new);
+            rs += pe[e];
+        }
+        rs = wave_sum16(rs);
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+        const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]), pack_bf16x2(pe[4], pe[5]),
+                          pack_bf16x2(pe[6], pe[7])};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) {
+            acc[c] *= alpha;
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.v[c]), pb, acc[c],
+                                                            0, 0, 0);
+        }
+    } else {
+        // ---- scores: one 16-token tile, row 4j+i <-> token 4j+i
+        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < C::NKC; ++c) {
+            const f32x4 kf = __builtin_bit_cast(f32x4, cur.k[0][c]);
+            const f32x4 qf = __builtin_bit_cast(f32x4, qr[c]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s4 = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[e], qf[e], s4, 0, 0, 0);
+        }
+        float s[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = s4[i] * scale_log2;
+        if (tail) {
+            const int base = tok0 + 4 * j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[i] = (base + i < L) ? s[i] : -INFINITY;
+#pragma unroll
+            for (int c = 0; c < C::NV; ++c)
+                cur.v[c] = u32x4{base + 0 < L ? cur.v[c][0] : 0u, base + 1 < L ? cur.v[c][1] : 0u,
+                                 base + 2 < L ? cur.v[c][2] : 0u, base + 3 < L ? cur.v[c][3] : 0u};
+        }
+        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mx = wave_max16(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float pe[4];
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pe[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
+            rs += pe[i];
+        }
+        rs = wave_sum16(rs);
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) {
+            acc[c] *= alpha;
+            const f32x4 vf = __builtin_bit_cast(f32x4, cur.v[c]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], pe[i], acc[c], 0, 0, 0);
+        }
+    }}
 
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(64) void decode_kernel(
@@ -208,118 +321,20 @@ __global__ __launch_bounds__(64) void decode_kernel(
             break;
         }
         const int nst = (cend - ctok + C::STEP - 1) / C::STEP;
+        // two-stage software pipeline: the next step's loads are in flight
+        // while the current step is computed; the loop body issues them
+        // unconditionally so the wait before each compute covers only the
+        // current step's loads
         StepRegs<BF16, D, BS> cur;
         issue_step<BF16, D, BS>(cur, kbase, vbase, blk_bytes, ent, blk0, nblk, ctok, L, n, j);
-        for (int st = 0; st < nst; ++st) {
-            const int tok0 = ctok + st * C::STEP;
+        int tok0 = ctok;
+        for (int st = 0; st + 1 < nst; ++st, tok0 += C::STEP) {
             StepRegs<BF16, D, BS> nxt;
-            if (st + 1 < nst)
-                issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, L, n,
-                                        j);
-            const bool tail = tok0 + C::STEP > L;
-            if constexpr (BF16) {
-                // ---- scores: two 16-token tiles, rows 4j+i <-> tokens 8j+i (tile a), 8j+4+i (tile b)
-                f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < C::NKC; ++c) {
-                    const bf16x8 qv = __builtin_bit_cast(bf16x8, qr[c]);
-                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[0][c]), qv, sa,
-                                                                0, 0, 0);
-                    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[1][c]), qv, sb,
-                                                                0, 0, 0);
-                }
-                float s[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    s[i] = sa[i] * scale_log2;
-                    s[4 + i] = sb[i] * scale_log2;
-                }
-                if (tail) {
-                    const int base = tok0 + 8 * j;
-                    uint32_t keep[4];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s[e] = (base + e < L) ? s[e] : -INFINITY;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        keep[w] = ((base + 2 * w < L) ? 0x0000ffffu : 0u) | ((base + 2 * w + 1 < L) ? 0xffff0000u : 0u);
-                    // values of masked tokens may be NaN: zero them (p = 0 would not)
-#pragma unroll
-                    for (int c = 0; c < C::NV; ++c)
-                        cur.v[c] = u32x4{cur.v[c][0] & keep[0], cur.v[c][1] & keep[1], cur.v[c][2] & keep[2],
-                                         cur.v[c][3] & keep[3]};
-                }
-                float mx = s[0];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-                mx = wave_max16(mx);
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                float pe[8];
-                float rs = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pe[e] = __builtin_amdgcn_exp2f(s[e] - m_new);
-                    rs += pe[e];
-                }
-                rs = wave_sum16(rs);
-                l_run = l_run * alpha + rs;
-                m_run = m_new;
-                const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]), pack_bf16x2(pe[4], pe[5]),
-                                  pack_bf16x2(pe[6], pe[7])};
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-                for (int c = 0; c < C::NV; ++c) {
-                    acc[c] *= alpha;
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.v[c]), pb, acc[c],
-                                                                    0, 0, 0);
-                }
-            } else {
-                // ---- scores: one 16-token tile, row 4j+i <-> token 4j+i
-                f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < C::NKC; ++c) {
-                    const f32x4 kf = __builtin_bit_cast(f32x4, cur.k[0][c]);
-                    const f32x4 qf = __builtin_bit_cast(f32x4, qr[c]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) s4 = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[e], qf[e], s4, 0, 0, 0);
-                }
-                float s[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[i] = s4[i] * scale_log2;
-                if (tail) {
-                    const int base = tok0 + 4 * j;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s[i] = (base + i < L) ? s[i] : -INFINITY;
-#pragma unroll
-                    for (int c = 0; c < C::NV; ++c)
-                        cur.v[c] = u32x4{base + 0 < L ? cur.v[c][0] : 0u, base + 1 < L ? cur.v[c][1] : 0u,
-                                         base + 2 < L ? cur.v[c][2] : 0u, base + 3 < L ? cur.v[c][3] : 0u};
-                }
-                float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-                mx = wave_max16(mx);
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                float pe[4];
-                float rs = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pe[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
-                    rs += pe[i];
-                }
-                rs = wave_sum16(rs);
-                l_run = l_run * alpha + rs;
-                m_run = m_new;
-#pragma unroll
-                for (int c = 0; c < C::NV; ++c) {
-                    acc[c] *= alpha;
-                    const f32x4 vf = __builtin_bit_cast(f32x4, cur.v[c]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], pe[i], acc[c], 0, 0, 0);
-                }
-            }
-            if (st + 1 < nst) cur = nxt;
+            issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, L, n, j);
+            compute_step<BF16, D, BS>(cur, qr, m_run, l_run, acc, tok0, L, j, scale_log2);
+            cur = nxt;
         }
+        compute_step<BF16, D, BS>(cur, qr, m_run, l_run, acc, tok0, L, j, scale_log2);
     }
 
     if (n >= G) return;

@@ -14,6 +14,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// 16-byte streaming load: marked non-temporal, for data read once (the
+// K/V pool during decode), so it does not displace reusable lines.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // float -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     uint32_t u = __float_as_uint(f);

@@ -24,7 +24,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
 
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_function():
     assert len(names) >= 15
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
-        assert hasattr(h, n), f"{n} declared in pa.h but not exported"
+        assert hasattr(h, n), f"{n} declared in include/ but not exported"
     assert sorted(n for n, _, _ in _lib.SIGNATURES) == names
 
 
@@ -242,3 +243,11 @@ def test_allocator_error_codes():
         pa.Allocator(3, 2, [0, 0, 1])
     h = pa.lib().pa_alloc_create(-1, 2, None)
     assert not h
+
+
+def test_stream_read_validation():
+    assert _l().pa_bench_stream_read(None, 16, fake(), 0, None) == pa.PA_ERR_INVALID_ARG
+    assert _l().pa_bench_stream_read(fake(0x10004), 16, fake(), 0, None) == pa.PA_ERR_INVALID_ARG
+    assert _l().pa_bench_stream_read(fake(), 17, fake(), 0, None) == pa.PA_ERR_INVALID_ARG
+    assert _l().pa_bench_stream_read(fake(), 16, fake(), -1, None) == pa.PA_ERR_INVALID_ARG
+    assert _l().pa_bench_stream_read(fake(), 0, fake(), 0, None) == pa.PA_OK
