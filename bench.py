@@ -36,7 +36,9 @@ if ROOT not in sys.path:
 from synthetic import make_workload  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
-DEFAULT_PARTITION = {"llama3_8b": 512, "llama_70b": 512, "prefix_share": 512}
+PARTITION_BALANCED = -1  # the library's balanced split (PA_PARTITION_BALANCED)
+DEFAULT_PARTITION = {"llama3_8b": PARTITION_BALANCED, "llama_70b": PARTITION_BALANCED,
+                     "prefix_share": PARTITION_BALANCED}
 WORKLOAD_TEXT = {
     "llama3_8b": "Llama-3-8B-shaped decode layer: batch 64, 32 q / 8 kv heads (GQA 4), d_head 128, block 16, "
                  "bf16, seq_lens U[512,4096], seeded random block permutation of a pool = demand + 10%",

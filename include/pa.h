@@ -124,20 +124,36 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
  *   dtype PA_BF16: bf16 inputs, bf16 matrix-core products, float32
  *   accumulation and softmax.  PA_F32: float32 throughout.
  *
- * Long contexts (split-sequence decode): with partition_size > 0 each
- * sequence is cut into partitions of partition_size tokens (a multiple of
- * 32 and of block_size, at most 64 * block_size); each partition's
- * attention output o_j, running max m_j and exp-sum l_j go to `workspace`
- * and a log-sum-exp merge combines them:
+ * Splitting a sequence across waves (split-sequence decode).  The result
+ * is the same attention whichever way a sequence is cut: each piece j
+ * yields its output o_j, maximum m_j and exp-sum l_j, and a log-sum-exp
+ * merge combines them:
  *   M = max_j m_j,  w_j = l_j * exp(m_j - M),  out = sum_j w_j o_j / sum_j w_j.
- * A sequence that fits one partition is written directly.  workspace must
- * hold pa_decode_workspace_bytes(...) bytes (device, 256-byte aligned); its
- * contents on entry do not matter.  With partition_size == 0 every
- * sequence is processed in one pass and workspace may be NULL.
+ *  partition_size == 0: no split; one wave per (sequence, kv-head).
+ *    workspace may be NULL.
+ *  partition_size > 0: fixed partitions of partition_size tokens (a
+ *    multiple of 32 and of block_size, at most 64 * block_size), merged by
+ *    a second kernel.  A sequence that fits one partition is written
+ *    directly.
+ *  partition_size == PA_PARTITION_BALANCED: the batch's token steps are
+ *    shared out evenly over a fixed grid of waves whatever the length mix;
+ *    a (sequence, kv-head) cut between waves is merged inside the same
+ *    kernel by the wave that finishes its last piece.  num_seqs <= 1024.
+ * workspace: device, 256-byte aligned, at least pa_decode_workspace_bytes()
+ * bytes.  Its first pa_decode_counter_bytes() bytes are counters that must
+ * be zero before the first PA_PARTITION_BALANCED call on that workspace
+ * (allocate it zero-filled); every call leaves them zero again, and the
+ * other modes do not touch them.  The rest is scratch whose contents on
+ * entry do not matter.  Calls sharing one workspace must not overlap.
  * ------------------------------------------------------------------------ */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t block_size, int32_t max_blocks_per_seq,
+#define PA_PARTITION_BALANCED (-1)
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                  int32_t partition_size);
+/* Bytes at the start of the workspace that hold the balanced split's
+ * counters (zero-filled once, see above). */
+size_t pa_decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads);
 
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* seq_lens,

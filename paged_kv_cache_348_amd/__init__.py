@@ -19,13 +19,14 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-from ._lib import (PA_BF16, PA_ERR_EXISTS, PA_ERR_INVALID_ARG, PA_ERR_LAUNCH, PA_ERR_NOT_FOUND, PA_ERR_OOM,
+from ._lib import (PA_BF16, PA_PARTITION_BALANCED, PA_ERR_EXISTS, PA_ERR_INVALID_ARG, PA_ERR_LAUNCH, PA_ERR_NOT_FOUND, PA_ERR_OOM,
                    PA_ERR_UNSUPPORTED, PA_F32, PA_OK, P_I32, P_I64, PAError, check, lib, status_string)
 
 __all__ = [
     "PAError", "Allocator", "cache_write", "copy_blocks", "decode", "decode_workspace_bytes", "new_kv_cache",
     "kv_cache_shapes", "logical_view", "stream_read", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_OOM",
-    "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "status_string", "lib",
+    "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
+    "new_workspace",
 ]
 
 
@@ -133,15 +134,25 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
                                bs, nb, _dtype_code(k_cache.dtype), _stream_ptr(stream)), "pa_copy_blocks")
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, block_size: int,
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
                            max_blocks_per_seq: int, partition_size: int) -> int:
-    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq,
-                                               partition_size))
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                               max_blocks_per_seq, partition_size))
+
+
+def new_workspace(nbytes: int, device="cuda"):
+    """A decode workspace: zero-filled, as the balanced split's counters require."""
+    return _torch().zeros(max(int(nbytes), 1), dtype=_torch().uint8, device=device)
 
 
 def decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale: float, out=None,
            partition_size: int = 0, workspace=None, stream=None):
-    """Decode attention; returns ``out`` [B, Hq, D] (q's dtype)."""
+    """Decode attention; returns ``out`` [B, Hq, D] (q's dtype).
+
+    partition_size: 0 single pass, > 0 fixed partitions, PA_PARTITION_BALANCED
+    (-1) the balanced split.  ``workspace`` (uint8 device tensor) must come
+    from new_workspace() or be otherwise zero-filled before its first use.
+    """
     torch = _torch()
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     if hkv != num_kv_heads:
@@ -158,11 +169,11 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale
     if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
         raise ValueError("out must match q")
     mb = block_tables.shape[1]
-    need = decode_workspace_bytes(B, hq, d, bs, mb, partition_size) if B else 0
+    need = decode_workspace_bytes(B, hq, hkv, d, bs, mb, partition_size) if B else 0
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = new_workspace(need, q.device)
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     check(lib().pa_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                           _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), hkv, float(scale),

@@ -18,6 +18,7 @@ P_I64 = ctypes.POINTER(ctypes.c_int64)
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_NOT_FOUND, PA_ERR_LAUNCH, PA_ERR_EXISTS = range(7)
 PA_F32, PA_BF16 = 0, 1
+PA_PARTITION_BALANCED = -1
 
 # (name, restype, argtypes) of every symbol include/pa.h and include/pa_bench.h declare
 SIGNATURES = [
@@ -26,7 +27,8 @@ SIGNATURES = [
                                  c_int32, c_int32, c_int32, c_void_p]),
     ("pa_copy_blocks", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                  c_int32, c_void_p]),
-    ("pa_decode_workspace_bytes", c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
+    ("pa_decode_workspace_bytes", c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
+    ("pa_decode_counter_bytes", c_size_t, [c_int32, c_int32]),
     ("pa_decode", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                             c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                             c_void_p, c_size_t]),

@@ -37,7 +37,8 @@ extern "C" pa_status pa_bench_stream_read(const void* buf, size_t bytes, uint32_
         return PA_ERR_INVALID_ARG;
     if (bytes == 0) return PA_OK;
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
     const int64_t nvec = (int64_t)(bytes / 16);
     int64_t wg = workgroups ? workgroups : (int64_t)cus;
     const int64_t need = (nvec + 255) / 256;

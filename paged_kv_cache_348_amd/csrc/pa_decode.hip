@@ -8,10 +8,11 @@
 //    the lookup sits inside the tile loop rather than in a separate gather
 //    (MCQ page, code sketch and its closing remark).
 //
-// Work decomposition.  One 64-lane wave per (partition, kv-head, sequence).
-// The wave walks its partition in steps of 32 tokens (bf16) or 16 tokens
-// (f32).  Each step loads the keys and values of its tokens straight from
-// the pool into registers with 16-byte loads whose per-lane placement is the
+// Work decomposition.  A 64-lane wave attends over a run of tokens of one
+// (sequence, kv-head) pair for all G query heads of that kv-head.  It walks
+// the run in steps of 32 tokens (bf16) or 16 tokens (f32).  Each step loads
+// the keys and values of its tokens straight from the pool into registers
+// with 16-byte non-temporal loads whose per-lane placement is the
 // matrix-core operand layout (the pool's tile layout is chosen for that,
 // see include/pa.h), so no key or value passes through LDS: every element
 // is used by exactly one lane.  The next step's loads are issued before the
@@ -37,12 +38,19 @@
 // valid as long as both operands use it; the loads below pick placements
 // that make every lane's 16 bytes contiguous in the pool.
 //
-// Long contexts: a sequence longer than one partition writes per-partition
-// (o_j, m_j, l_j) to the workspace and merge_kernel combines them with the
-// log-sum-exp rule.  m_j is kept in the base-2 scaled domain
-// (m_j = max_p scale*log2(e)*score), so the merge weights are
-// w_j = l_j * 2^(m_j - M).
+// Which runs the waves take:
+//  - single pass: one wave per (sequence, kv-head);
+//  - fixed partitions: one wave per (kv-head, partition, sequence); each
+//    partition leaves (o_j, m_j, l_j) in the workspace and merge_kernel
+//    combines them with the log-sum-exp rule
+//      M = max_j m_j,  w_j = l_j 2^(m_j - M),  out = sum_j w_j o_j / sum_j w_j
+//    (m_j is kept in the base-2 scaled domain, max_p scale*log2(e)*score);
+//  - balanced split: a fixed grid of waves, each taking an equal share of
+//    all the token steps of the batch (decode_balanced_kernel), with the
+//    pieces of a cut (sequence, kv-head) merged by the same rule inside the
+//    kernel.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -64,6 +72,7 @@ struct DecodeCfg {
     static constexpr int VT = BF16 ? 8 : 4;             // tokens in one value load
     static constexpr int NE = STEP / BS > 0 ? STEP / BS : 1;  // table entries a step touches
     static constexpr int64_t TILE = (int64_t)D * BS;    // elements of one (block, head) tile
+    typedef u32x4 QRegs[NKC];                           // query operand of one lane
     static_assert(D % 32 == 0 && BS % 8 == 0, "shape");
 };
 
@@ -251,8 +260,117 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
             for (int i = 0; i < 4; ++i)
                 acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[i], pe[i], acc[c], 0, 0, 0);
         }
-    }}
+    }
+}
 
+// Running state of one wave over a run of tokens of one (sequence, kv-head):
+// online-softmax maximum and sum per head column, the unnormalised PV
+// accumulator, and whether a bad block-table entry was met.
+template <bool BF16, int D, int BS>
+struct RunState {
+    float m;
+    float l;
+    f32x4 acc[DecodeCfg<BF16, D, BS>::NV];
+    bool bad;
+};
+
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void run_init(RunState<BF16, D, BS>& S) {
+    S.m = -INFINITY;
+    S.l = 0.0f;
+#pragma unroll
+    for (int c = 0; c < DecodeCfg<BF16, D, BS>::NV; ++c) S.acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    S.bad = false;
+}
+
+// Query operand of kv-head g's G query heads: lane (n, j) holds 16-byte
+// chunks 4c + j of head g*G + n (zero for the padding columns n >= G).
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void load_q(typename DecodeCfg<BF16, D, BS>::QRegs& qr, const void* __restrict__ q_,
+                                       int64_t row, int n, int j, int G) {
+    using C = DecodeCfg<BF16, D, BS>;
+    const char* qp = reinterpret_cast<const char*>(q_) + row * D * C::ES;
+#pragma unroll
+    for (int c = 0; c < C::NKC; ++c) qr[c] = (n < G) ? ld16(qp + (int64_t)(4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Attention over tokens [start, end) of one sequence (0 <= start < end <= L)
+// for one kv-head: the block table is walked in chunks of kTableChunk
+// entries (one per lane, read back with readlane), and inside a chunk the
+// tokens are streamed in steps through a two-stage load pipeline.  The loop
+// body issues the next step's loads unconditionally, so the wait before each
+// compute covers only the current step's loads.
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void attend_range(RunState<BF16, D, BS>& S,
+                                             const u32x4 (&qr)[DecodeCfg<BF16, D, BS>::NKC],
+                                             const char* __restrict__ kbase, const char* __restrict__ vbase,
+                                             int64_t blk_bytes, const int32_t* __restrict__ trow, int num_blocks,
+                                             int start, int end, int L, int lane, int n, int j, float scale_log2) {
+    using C = DecodeCfg<BF16, D, BS>;
+    for (int ctok = start; ctok < end; ctok += kTableChunk * BS) {
+        const int cend = min(ctok + kTableChunk * BS, end);
+        const int blk0 = ctok / BS;
+        const int nblk = (cend - 1) / BS - blk0 + 1;
+        const int32_t ent = (lane < nblk) ? trow[blk0 + lane] : 0;
+        if (__any(lane < nblk && (ent < 0 || ent >= num_blocks))) {
+            S.bad = true;
+            return;
+        }
+        const int nst = (cend - ctok + C::STEP - 1) / C::STEP;
+        StepRegs<BF16, D, BS> cur;
+        issue_step<BF16, D, BS>(cur, kbase, vbase, blk_bytes, ent, blk0, nblk, ctok, L, n, j);
+        int tok0 = ctok;
+        for (int st = 0; st + 1 < nst; ++st, tok0 += C::STEP) {
+            StepRegs<BF16, D, BS> nxt;
+            issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, L, n, j);
+            compute_step<BF16, D, BS>(cur, qr, S.m, S.l, S.acc, tok0, L, j, scale_log2);
+            cur = nxt;
+        }
+        compute_step<BF16, D, BS>(cur, qr, S.m, S.l, S.acc, tok0, L, j, scale_log2);
+    }
+}
+
+// Normalise and store the G output rows of one (sequence, kv-head) starting
+// at row `row0` of out; a bad table entry gives NaN rows.
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void store_out(void* __restrict__ out_, int64_t row0, const RunState<BF16, D, BS>& S,
+                                          int n, int j, int G) {
+    using C = DecodeCfg<BF16, D, BS>;
+    if (n >= G) return;
+    const float inv = S.bad ? __builtin_nanf("") : 1.0f / S.l;
+    const int64_t orow = (row0 + n) * D;
+#pragma unroll
+    for (int c = 0; c < C::NV; ++c) {
+        const int d0 = 16 * c + 4 * j;
+        if constexpr (BF16) {
+            uint2 w;
+            w.x = pack_bf16x2(S.acc[c][0] * inv, S.acc[c][1] * inv);
+            w.y = pack_bf16x2(S.acc[c][2] * inv, S.acc[c][3] * inv);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out_) + orow + d0) = w;
+        } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out_) + orow + d0) = S.acc[c] * inv;
+        }
+    }
+}
+
+// Fill `nrows` output rows from `row0` with v (zero rows for empty
+// sequences, NaN rows for lengths the block table cannot hold).
+template <bool BF16, int D>
+__device__ __forceinline__ void fill_rows(void* __restrict__ out_, int64_t row0, int nrows, float v, int lane) {
+    for (int i = lane; i < nrows * D; i += 64) {
+        const int64_t o = row0 * D + i;
+        if constexpr (BF16)
+            reinterpret_cast<uint16_t*>(out_)[o] = (uint16_t)bf16_bits_rne(v);
+        else
+            reinterpret_cast<float*>(out_)[o] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------- fixed partitions
+
+// One wave per (kv-head, partition, sequence).  A sequence that fits one
+// partition is written directly; otherwise each partition writes its
+// normalised output o_j, maximum m_j and sum l_j for merge_kernel.
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(64) void decode_kernel(
     const void* __restrict__ q_, const void* __restrict__ kc_, const void* __restrict__ vc_,
@@ -271,100 +389,36 @@ __global__ __launch_bounds__(64) void decode_kernel(
     const bool len_ok = L > 0 && (int64_t)L <= (int64_t)max_blocks * BS;
     const int nparts = len_ok ? (L + PS - 1) / PS : 1;
     if (p >= nparts) return;
-    const bool direct = nparts == 1;
-    const int h = g * G + n;
-
+    const int64_t row0 = (int64_t)b * Hq + g * G;
     if (!len_ok) {
-        // empty sequence: zero row; a length the table cannot hold: NaN row
-        const float fill = (L <= 0) ? 0.0f : __builtin_nanf("");
-        for (int i = lane; i < G * D; i += 64) {
-            const int64_t o = ((int64_t)b * Hq + g * G) * D + i;
-            if constexpr (BF16)
-                reinterpret_cast<uint16_t*>(out_)[o] = (uint16_t)bf16_bits_rne(fill);
-            else
-                reinterpret_cast<float*>(out_)[o] = fill;
-        }
+        fill_rows<BF16, D>(out_, row0, G, L <= 0 ? 0.0f : __builtin_nanf(""), lane);
         return;
     }
-
     const int start = p * PS;
     const int end = min(start + PS, L);
     const int64_t blk_bytes = (int64_t)Hkv * C::TILE * C::ES;
-    const char* kbase = reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES;
-    const char* vbase = reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES;
-    const int32_t* trow = tables + (int64_t)b * max_blocks;
-
-    // query operand: lane holds 16-byte chunks 4*c + j of head n (zero for padding heads)
     u32x4 qr[C::NKC];
-    {
-        const char* qp = reinterpret_cast<const char*>(q_) + ((int64_t)b * Hq + h) * D * C::ES;
-#pragma unroll
-        for (int c = 0; c < C::NKC; ++c) {
-            qr[c] = (n < G) ? ld16(qp + (int64_t)(4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
-        }
+    load_q<BF16, D, BS>(qr, q_, row0 + n, n, j, G);
+    RunState<BF16, D, BS> S;
+    run_init(S);
+    attend_range<BF16, D, BS>(S, qr, reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES,
+                              reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES, blk_bytes,
+                              tables + (int64_t)b * max_blocks, num_blocks, start, end, L, lane, n, j, scale_log2);
+    if (nparts == 1) {
+        store_out<BF16, D, BS>(out_, row0, S, n, j, G);
+        return;
     }
-
-    float m_run = -INFINITY;
-    float l_run = 0.0f;
-    f32x4 acc[C::NV];
-#pragma unroll
-    for (int c = 0; c < C::NV; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool bad = false;
-
-    for (int ctok = start; ctok < end; ctok += kTableChunk * BS) {
-        const int cend = min(ctok + kTableChunk * BS, end);
-        const int blk0 = ctok / BS;
-        const int nblk = (cend - 1) / BS - blk0 + 1;
-        const int32_t ent = (lane < nblk) ? trow[blk0 + lane] : 0;
-        if (__any(lane < nblk && (ent < 0 || ent >= num_blocks))) {
-            bad = true;
-            break;
-        }
-        const int nst = (cend - ctok + C::STEP - 1) / C::STEP;
-        // two-stage software pipeline: the next step's loads are in flight
-        // while the current step is computed; the loop body issues them
-        // unconditionally so the wait before each compute covers only the
-        // current step's loads
-        StepRegs<BF16, D, BS> cur;
-        issue_step<BF16, D, BS>(cur, kbase, vbase, blk_bytes, ent, blk0, nblk, ctok, L, n, j);
-        int tok0 = ctok;
-        for (int st = 0; st + 1 < nst; ++st, tok0 += C::STEP) {
-            StepRegs<BF16, D, BS> nxt;
-            issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, L, n, j);
-            compute_step<BF16, D, BS>(cur, qr, m_run, l_run, acc, tok0, L, j, scale_log2);
-            cur = nxt;
-        }
-        compute_step<BF16, D, BS>(cur, qr, m_run, l_run, acc, tok0, L, j, scale_log2);
-    }
-
     if (n >= G) return;
-    const float nanv = __builtin_nanf("");
-    const float inv = bad ? nanv : 1.0f / l_run;
-    if (direct) {
-        const int64_t orow = ((int64_t)b * Hq + h) * D;
+    const float inv = S.bad ? __builtin_nanf("") : 1.0f / S.l;
+    const int64_t prow = (row0 + n) * P_max + p;
 #pragma unroll
-        for (int c = 0; c < C::NV; ++c) {
-            const int d0 = 16 * c + 4 * j;
-            if constexpr (BF16) {
-                uint2 w;
-                w.x = pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv);
-                w.y = pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv);
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out_) + orow + d0) = w;
-            } else {
-                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out_) + orow + d0) = acc[c] * inv;
-            }
-        }
-    } else {
-        const int64_t prow = ((int64_t)b * Hq + h) * P_max + p;
-#pragma unroll
-        for (int c = 0; c < C::NV; ++c) {
-            const int d0 = 16 * c + 4 * j;
-            *reinterpret_cast<f32x4*>(part_o + prow * D + d0) = acc[c] * inv;
-        }
-        if (j == 0) {
-            part_ml[2 * prow] = bad ? 0.0f : m_run;
-            part_ml[2 * prow + 1] = bad ? 1.0f : l_run;
-        }
+    for (int c = 0; c < C::NV; ++c) {
+        const int d0 = 16 * c + 4 * j;
+        *reinterpret_cast<f32x4*>(part_o + prow * D + d0) = S.acc[c] * inv;
+    }
+    if (j == 0) {
+        part_ml[2 * prow] = S.bad ? 0.0f : S.m;
+        part_ml[2 * prow + 1] = S.bad ? 1.0f : S.l;
     }
 }
 
@@ -420,6 +474,206 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     }
 }
 
+// ---------------------------------------------------------------------------- balanced split
+
+constexpr int kBalancedMaxSeqs = 1024;   // sequences a balanced call may hold
+constexpr int kBalancedMaxWaves = 2048;  // waves (and partial-slot pairs) of a balanced call
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Two floats written / read as one 64-bit agent-scope atomic access: the
+// access goes to the device-coherent level, so a wave on another XCD that
+// reads it after a later counter update sees it.
+__device__ __forceinline__ void coherent_store(uint64_t* p, float lo, float hi) {
+    const uint64_t v = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 coherent_load(const uint64_t* p) {
+    const uint64_t v = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// Wave (of nw) whose step range holds global step x; wave w covers
+// [S*w/nw, S*(w+1)/nw).
+__device__ __forceinline__ int wave_of_step(int64_t x, int64_t S, int nw) {
+    return (int)(((x + 1) * nw - 1) / S);
+}
+
+// Balanced split ("stream-K" over the attention's token steps).
+//
+// The work is the sequence of segments (b, g), b-major, each of
+// ceil(L_b / STEP) steps.  Wave w of nw takes the global steps
+// [S*w/nw, S*(w+1)/nw), so every wave reads the same number of key/value
+// bytes whatever the length mix.  A segment wholly inside one wave is
+// written directly.  A segment cut by wave boundaries leaves one partial
+// (unnormalised accumulator, running maximum and sum) per piece in the
+// workspace; each piece then bumps the segment's counter, and the wave that
+// brings it to the piece count merges the pieces with the log-sum-exp rule,
+// writes the rows and puts the counter back to zero.  No wave waits for
+// another.
+template <bool BF16, int D, int BS>
+__global__ __launch_bounds__(64) void decode_balanced_kernel(
+    const void* __restrict__ q_, const void* __restrict__ kc_, const void* __restrict__ vc_,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ lens, void* __restrict__ out_,
+    float* __restrict__ slot_o, float* __restrict__ slot_ml, int32_t* __restrict__ counters, int B, int Hq,
+    int Hkv, int G, int max_blocks, int num_blocks, float scale_log2) {
+    using C = DecodeCfg<BF16, D, BS>;
+    __shared__ int64_t s_first[kBalancedMaxSeqs];  // global step where sequence b's segments start
+    __shared__ int32_t s_steps[kBalancedMaxSeqs];  // steps per segment of sequence b (0: no work)
+    const int lane = threadIdx.x;
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    const int w = blockIdx.x;
+
+    // 1. step counts of every sequence and their prefix sums (each wave
+    //    computes the same table; the length loads are issued together)
+    constexpr int NCH = kBalancedMaxSeqs / 64;
+    int32_t lv[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int b = 64 * c + lane;
+        lv[c] = (b < B) ? lens[b] : 0;
+    }
+    int64_t S = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (64 * c >= B) break;
+        const int b = 64 * c + lane;
+        const int L = lv[c];
+        const bool ok = b < B && L > 0 && (int64_t)L <= (int64_t)max_blocks * BS;
+        const int st = ok ? (L + C::STEP - 1) / C::STEP : 0;
+        const int64_t v = (int64_t)st * Hkv;
+        const int64_t incl = wave_incl_scan(v, lane);
+        if (b < B) {
+            s_first[b] = S + incl - v;
+            s_steps[b] = st;
+        }
+        S += __shfl(incl, 63, 64);
+    }
+    __syncthreads();
+
+    // 2. rows no segment covers: empty sequences (zeros) and lengths the
+    //    table cannot hold (NaN)
+    for (int b = w; b < B; b += gridDim.x) {
+        if (s_steps[b] == 0) {
+            const int L = lens[b];
+            fill_rows<BF16, D>(out_, (int64_t)b * Hq, Hq, L <= 0 ? 0.0f : __builtin_nanf(""), lane);
+        }
+    }
+    const int nw = (int)min((int64_t)gridDim.x, S);
+    if (w >= nw) return;
+    const int64_t wbeg = S * w / nw;
+    const int64_t wend = S * (w + 1) / nw;
+
+    // 3. the sequence holding step wbeg: the last b with s_first[b] <= wbeg
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_first[mid] <= wbeg) lo = mid;
+        else hi = mid - 1;
+    }
+    int b = lo;
+
+    const int64_t blk_bytes = (int64_t)Hkv * C::TILE * C::ES;
+    int64_t pos = wbeg;
+    while (pos < wend) {
+        while (pos >= s_first[b] + (int64_t)s_steps[b] * Hkv) ++b;  // skip finished / empty sequences
+        const int nst = s_steps[b];
+        const int g = (int)((pos - s_first[b]) / nst);
+        const int64_t seg0 = s_first[b] + (int64_t)g * nst;
+        const int64_t seg1 = seg0 + nst;
+        const int64_t pend = min(seg1, wend);
+        const int L = lens[b];
+        const int t0 = (int)(pos - seg0) * C::STEP;
+        const int t1 = min((int)(pend - seg0) * C::STEP, L);
+        const int64_t row0 = (int64_t)b * Hq + g * G;
+
+        u32x4 qr[C::NKC];
+        load_q<BF16, D, BS>(qr, q_, row0 + n, n, j, G);
+        RunState<BF16, D, BS> St;
+        run_init(St);
+        attend_range<BF16, D, BS>(St, qr, reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES,
+                                  reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES, blk_bytes,
+                                  tables + (int64_t)b * max_blocks, num_blocks, t0, t1, L, lane, n, j, scale_log2);
+
+        if (pos == seg0 && pend == seg1) {
+            store_out<BF16, D, BS>(out_, row0, St, n, j, G);
+        } else {
+            // partial of this piece: slot (w, 0) if it holds the wave's first step, else (w, 1).
+            // Partials and the counter are read and written with agent-scope atomic
+            // accesses, which go to the device-coherent level and bypass each XCD's L2,
+            // so no cache-wide write-back or invalidate is needed.
+            const int64_t slot = 2 * (int64_t)w + (pos == wbeg ? 0 : 1);
+            if (n < G) {
+                uint64_t* po = reinterpret_cast<uint64_t*>(slot_o + (slot * G + n) * D);
+#pragma unroll
+                for (int c = 0; c < C::NV; ++c) {
+                    const f32x4 a = St.bad ? f32x4{NAN, NAN, NAN, NAN} : St.acc[c];
+                    const int e = (16 * c + 4 * j) / 2;
+                    coherent_store(po + e, a[0], a[1]);
+                    coherent_store(po + e + 1, a[2], a[3]);
+                }
+                if (j == 0)
+                    coherent_store(reinterpret_cast<uint64_t*>(slot_ml + (slot * G + n) * 2), St.bad ? 0.0f : St.m,
+                                   St.bad ? 1.0f : St.l);
+            }
+            const int w0 = wave_of_step(seg0, S, nw);
+            const int w1 = wave_of_step(seg1 - 1, S, nw);
+            int32_t* cnt = counters + (int64_t)b * Hkv + g;
+            // the partial must be complete at the coherent level before counting in
+            __builtin_amdgcn_s_waitcnt(0);
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __shfl(old, 0, 64);
+            if (old == w1 - w0) {
+                // last piece in: merge every piece of the segment
+                if (n < G) {
+                    float M = -INFINITY;
+                    for (int k = w0; k <= w1; ++k) {
+                        const int64_t sk = 2 * (int64_t)k + ((k == w0 && seg0 != S * k / nw) ? 1 : 0);
+                        M = fmaxf(M, coherent_load(reinterpret_cast<uint64_t*>(slot_ml + (sk * G + n) * 2)).x);
+                    }
+                    float den = 0.0f;
+                    f32x4 num[C::NV];
+#pragma unroll
+                    for (int c = 0; c < C::NV; ++c) num[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int k = w0; k <= w1; ++k) {
+                        const int64_t sk = 2 * (int64_t)k + ((k == w0 && seg0 != S * k / nw) ? 1 : 0);
+                        const float2 ml = coherent_load(reinterpret_cast<uint64_t*>(slot_ml + (sk * G + n) * 2));
+                        const float wt = __builtin_amdgcn_exp2f(ml.x - M);
+                        den += wt * ml.y;
+                        uint64_t* po = reinterpret_cast<uint64_t*>(slot_o + (sk * G + n) * D);
+#pragma unroll
+                        for (int c = 0; c < C::NV; ++c) {
+                            const int e = (16 * c + 4 * j) / 2;
+                            const float2 lo = coherent_load(po + e), hi = coherent_load(po + e + 1);
+                            num[c] += wt * f32x4{lo.x, lo.y, hi.x, hi.y};
+                        }
+                    }
+                    RunState<BF16, D, BS> Mg;
+                    Mg.m = M;
+                    Mg.l = den;
+                    Mg.bad = false;
+#pragma unroll
+                    for (int c = 0; c < C::NV; ++c) Mg.acc[c] = num[c];
+                    store_out<BF16, D, BS>(out_, row0, Mg, n, j, G);
+                }
+                if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        pos = pend;
+    }
+}
+
 }  // namespace pa
 
 // ---------------------------------------------------------------------------- host side
@@ -431,7 +685,12 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Effective partition length and partition count for a call.
+// Workspace layout (every mode): [counters | partials].  The counter region
+// (int32 per (sequence, kv-head), used by the balanced split) comes first so
+// that other modes never overwrite it.
+inline size_t counter_bytes(int64_t B, int64_t Hkv) { return align_up((size_t)(B * Hkv) * sizeof(int32_t)); }
+
+// Effective partition length and partition count of the fixed-partition modes.
 inline void partition_plan(int32_t block_size, int32_t max_blocks, int32_t partition_size, int64_t* ps,
                            int64_t* pmax) {
     const int64_t cap = (int64_t)max_blocks * block_size;
@@ -445,51 +704,81 @@ inline void partition_plan(int32_t block_size, int32_t max_blocks, int32_t parti
     }
 }
 
+// Waves of a balanced call: kWavesPerCU per compute unit of the current device.
+// Measured on MI355X (Llama-3-8B-shaped batch): 2 per CU reads fastest; 4
+// is ~3 % slower and more than 4 no longer fit in one round.
+constexpr int kWavesPerCU = 2;
+int balanced_waves() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached[dev] = std::min(pa::kBalancedMaxWaves, kWavesPerCU * cus);
+    }
+    return cached[dev];
+}
+
+struct Launch {
+    const void *q, *kc, *vc;
+    const int32_t *tables, *lens;
+    void* out;
+    float *po, *pml;
+    int32_t* counters;
+    int B, Hq, Hkv, max_blocks, num_blocks, PS, P_max;
+    bool balanced;
+    float sl2;
+    hipStream_t stream;
+};
+
 template <bool BF16, int D, int BS>
-hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* tables,
-                         const int32_t* lens, void* out, float* po, float* pml, int B, int Hq, int Hkv,
-                         int max_blocks, int num_blocks, int PS, int P_max, float scale_log2,
-                         hipStream_t stream) {
-    dim3 grid((unsigned)Hkv, (unsigned)P_max, (unsigned)B);
-    hipLaunchKernelGGL((pa::decode_kernel<BF16, D, BS>), grid, dim3(64), 0, stream, q, kc, vc, tables, lens, out,
-                       po, pml, Hq, Hkv, Hq / Hkv, max_blocks, num_blocks, PS, P_max, scale_log2);
+hipError_t launch_decode(const Launch& a) {
+    const int G = a.Hq / a.Hkv;
+    if (a.balanced) {
+        hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS>), dim3((unsigned)balanced_waves()), dim3(64), 0,
+                           a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml, a.counters, a.B, a.Hq,
+                           a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2);
+        return hipGetLastError();
+    }
+    dim3 grid((unsigned)a.Hkv, (unsigned)a.P_max, (unsigned)a.B);
+    hipLaunchKernelGGL((pa::decode_kernel<BF16, D, BS>), grid, dim3(64), 0, a.stream, a.q, a.kc, a.vc, a.tables,
+                       a.lens, a.out, a.po, a.pml, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.PS, a.P_max, a.sl2);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || P_max <= 1) return e;
-    hipLaunchKernelGGL((pa::merge_kernel<BF16, D>), dim3((unsigned)Hq, (unsigned)B), dim3(256), 0, stream, po, pml,
-                       lens, out, Hq, max_blocks, BS, PS, P_max);
+    if (e != hipSuccess || a.P_max <= 1) return e;
+    hipLaunchKernelGGL((pa::merge_kernel<BF16, D>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(256), 0, a.stream, a.po,
+                       a.pml, a.lens, a.out, a.Hq, a.max_blocks, BS, a.PS, a.P_max);
     return hipGetLastError();
 }
 
 template <bool BF16, int D>
-hipError_t dispatch_bs(int BS, const void* q, const void* kc, const void* vc, const int32_t* tables,
-                       const int32_t* lens, void* out, float* po, float* pml, int B, int Hq, int Hkv,
-                       int max_blocks, int num_blocks, int PS, int P_max, float sl2, hipStream_t s) {
+hipError_t dispatch_bs(int BS, const Launch& a) {
     switch (BS) {
-        case 8:
-            return launch_decode<BF16, D, 8>(q, kc, vc, tables, lens, out, po, pml, B, Hq, Hkv, max_blocks,
-                                             num_blocks, PS, P_max, sl2, s);
-        case 16:
-            return launch_decode<BF16, D, 16>(q, kc, vc, tables, lens, out, po, pml, B, Hq, Hkv, max_blocks,
-                                              num_blocks, PS, P_max, sl2, s);
-        default:
-            return launch_decode<BF16, D, 32>(q, kc, vc, tables, lens, out, po, pml, B, Hq, Hkv, max_blocks,
-                                              num_blocks, PS, P_max, sl2, s);
+        case 8: return launch_decode<BF16, D, 8>(a);
+        case 16: return launch_decode<BF16, D, 16>(a);
+        default: return launch_decode<BF16, D, 32>(a);
     }
 }
 
 }  // namespace
 
-extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                            int32_t block_size, int32_t max_blocks_per_seq,
+extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                             int32_t partition_size) {
-    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
-        partition_size < 0)
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq < 0 || partition_size < PA_PARTITION_BALANCED)
         return 0;
+    const size_t cnt = counter_bytes(num_seqs, num_kv_heads);
+    if (partition_size == PA_PARTITION_BALANCED) {
+        const size_t slots = 2 * (size_t)pa::kBalancedMaxWaves * (size_t)(num_q_heads / num_kv_heads);
+        return cnt + align_up(slots * head_dim * sizeof(float)) + align_up(slots * 2 * sizeof(float));
+    }
     int64_t ps, pmax;
     partition_plan(block_size, max_blocks_per_seq, partition_size, &ps, &pmax);
     if (pmax <= 1) return 0;
     const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)pmax;
-    return align_up(rows * head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+    return cnt + align_up(rows * head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
 }
 
 extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -499,7 +788,7 @@ extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v
                                int32_t max_blocks_per_seq, pa_dtype dtype, int32_t partition_size,
                                void* workspace, size_t workspace_bytes) {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
-        partition_size < 0 || !std::isfinite(scale))
+        partition_size < PA_PARTITION_BALANCED || !std::isfinite(scale))
         return PA_ERR_INVALID_ARG;
     if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
     if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
@@ -511,41 +800,58 @@ extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v
     if (partition_size > 0 &&
         (partition_size % 32 != 0 || partition_size % block_size != 0 || partition_size > 64 * block_size))
         return PA_ERR_UNSUPPORTED;
+    const bool balanced = partition_size == PA_PARTITION_BALANCED;
+    if (balanced && num_seqs > pa::kBalancedMaxSeqs) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
         return PA_ERR_INVALID_ARG;
 
-    int64_t ps, pmax;
-    partition_plan(block_size, max_blocks_per_seq, partition_size, &ps, &pmax);
-    if (pmax > 65535) return PA_ERR_UNSUPPORTED;
-    float* po = nullptr;
-    float* pml = nullptr;
-    if (pmax > 1) {
-        const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size,
+    int64_t ps = 0, pmax = 1;
+    if (!balanced) {
+        partition_plan(block_size, max_blocks_per_seq, partition_size, &ps, &pmax);
+        if (pmax > 65535) return PA_ERR_UNSUPPORTED;
+    }
+    Launch a{};
+    if (balanced || pmax > 1) {
+        const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                                       max_blocks_per_seq, partition_size);
         if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
             return PA_ERR_INVALID_ARG;
-        const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)pmax;
-        po = reinterpret_cast<float*>(workspace);
-        pml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align_up(rows * head_dim * sizeof(float)));
+        char* ws = reinterpret_cast<char*>(workspace);
+        const size_t cnt = counter_bytes(num_seqs, num_kv_heads);
+        const size_t rows = balanced ? 2 * (size_t)pa::kBalancedMaxWaves * (size_t)(num_q_heads / num_kv_heads)
+                                     : (size_t)num_seqs * num_q_heads * (size_t)pmax;
+        a.counters = reinterpret_cast<int32_t*>(ws);
+        a.po = reinterpret_cast<float*>(ws + cnt);
+        a.pml = reinterpret_cast<float*>(ws + cnt + align_up(rows * head_dim * sizeof(float)));
     }
-    const float sl2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.tables = block_tables;
+    a.lens = seq_lens;
+    a.out = out;
+    a.B = num_seqs;
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.PS = (int)ps;
+    a.P_max = (int)pmax;
+    a.balanced = balanced;
+    a.sl2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+    a.stream = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
-    const int B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads, MB = max_blocks_per_seq, NB = num_blocks;
-    const int PS = (int)ps, PM = (int)pmax;
-    if (dtype == PA_BF16) {
-        e = head_dim == 128 ? dispatch_bs<true, 128>(block_size, q, k_cache, v_cache, block_tables, seq_lens, out, po,
-                                                     pml, B, Hq, Hkv, MB, NB, PS, PM, sl2, s)
-                            : dispatch_bs<true, 64>(block_size, q, k_cache, v_cache, block_tables, seq_lens, out, po,
-                                                    pml, B, Hq, Hkv, MB, NB, PS, PM, sl2, s);
-    } else {
-        e = head_dim == 128 ? dispatch_bs<false, 128>(block_size, q, k_cache, v_cache, block_tables, seq_lens, out,
-                                                      po, pml, B, Hq, Hkv, MB, NB, PS, PM, sl2, s)
-                            : dispatch_bs<false, 64>(block_size, q, k_cache, v_cache, block_tables, seq_lens, out, po,
-                                                     pml, B, Hq, Hkv, MB, NB, PS, PM, sl2, s);
-    }
+    if (dtype == PA_BF16)
+        e = head_dim == 128 ? dispatch_bs<true, 128>(block_size, a) : dispatch_bs<true, 64>(block_size, a);
+    else
+        e = head_dim == 128 ? dispatch_bs<false, 128>(block_size, a) : dispatch_bs<false, 64>(block_size, a);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+extern "C" size_t pa_decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads) {
+    if (num_seqs <= 0 || num_kv_heads <= 0) return 0;
+    return counter_bytes(num_seqs, num_kv_heads);
 }

@@ -16,7 +16,7 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-from . import Allocator, cache_write, copy_blocks, decode, decode_workspace_bytes, new_kv_cache
+from . import Allocator, cache_write, copy_blocks, decode, decode_workspace_bytes, new_kv_cache, new_workspace
 
 
 def _torch():
@@ -65,9 +65,10 @@ class DeviceBatch:
         w = self.workload
         ps = self.partition_size if partition_size is None else partition_size
         ws = self.workspace
-        need = decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim, w.block_size, self.max_blocks, ps)
+        need = decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                      self.max_blocks, ps)
         if need and (ws is None or ws.numel() < need):
-            ws = _torch().empty(need, dtype=_torch().uint8, device=self.q.device)
+            ws = new_workspace(need, self.q.device)
             if partition_size is None:
                 self.workspace = ws
         return decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.num_kv_heads, w.scale,
@@ -193,8 +194,9 @@ def build_device_batch(w, device="cuda", partition_size: Optional[int] = None, n
     dv = np.concatenate(dv) if dv else np.empty(shape, w.np_dtype)
 
     ps = w.partition_size if partition_size is None else partition_size
-    need = decode_workspace_bytes(w.batch, w.num_q_heads, w.head_dim, w.block_size, width, ps) if w.batch else 0
-    ws = torch.empty(need, dtype=torch.uint8, device=device) if need else None
+    need = (decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, width, ps)
+            if w.batch else 0)
+    ws = new_workspace(need, device) if need else None
     q = to_device(w.q, w.dtype, device)
     return DeviceBatch(
         workload=w, allocator=alloc, q=q, k_cache=kc, v_cache=vc,

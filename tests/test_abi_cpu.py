@@ -107,6 +107,9 @@ def decode_call(**kw):
     (dict(q=None), pa.PA_ERR_INVALID_ARG),
     (dict(out=fake(0x10004)), pa.PA_ERR_INVALID_ARG),
     (dict(B=0, q=None, kc=None, vc=None, bt=None, sl=None, out=None), pa.PA_OK),
+    (dict(ps=-1, ws=None), pa.PA_ERR_INVALID_ARG),                   # balanced split needs a workspace
+    (dict(ps=-1, B=1025), pa.PA_ERR_UNSUPPORTED),                     # too many sequences to balance
+    (dict(ps=-2), pa.PA_ERR_INVALID_ARG),
 ])
 def test_decode_rejects_bad_arguments(kw, expect):
     assert decode_call(**kw) == expect
@@ -114,11 +117,18 @@ def test_decode_rejects_bad_arguments(kw, expect):
 
 def test_workspace_size_formula():
     # partitions of 512 over 8 blocks of 16 = 128 tokens: one partition, no workspace
-    assert pa.decode_workspace_bytes(4, 32, 128, 16, 8, 512) == 0
-    assert pa.decode_workspace_bytes(4, 32, 128, 16, 8, 0) == 0
-    n = pa.decode_workspace_bytes(64, 32, 128, 16, 256, 512)
+    assert pa.decode_workspace_bytes(4, 32, 8, 128, 16, 8, 512) == 0
+    assert pa.decode_workspace_bytes(4, 32, 8, 128, 16, 8, 0) == 0
+    cnt = _l().pa_decode_counter_bytes(64, 8)
+    assert cnt >= 64 * 8 * 4 and cnt % 256 == 0
+    n = pa.decode_workspace_bytes(64, 32, 8, 128, 16, 256, 512)
     rows = 64 * 32 * 8
-    assert n >= rows * 128 * 4 + rows * 2 * 4 and n % 256 == 0
+    assert n >= cnt + rows * 128 * 4 + rows * 2 * 4 and n % 256 == 0
+    # balanced split: counters plus two partial slots of G heads per wave
+    nb = pa.decode_workspace_bytes(64, 32, 8, 128, 16, 256, pa.PA_PARTITION_BALANCED)
+    assert nb >= cnt + 2 * 2048 * 4 * (128 + 2) * 4 and nb % 256 == 0
+    assert pa.decode_workspace_bytes(64, 32, 8, 128, 16, 256, -2) == 0
+    assert pa.decode_workspace_bytes(64, 30, 8, 128, 16, 256, 512) == 0  # heads not grouped evenly
 
 
 # ---------------------------------------------------------------- allocator parity

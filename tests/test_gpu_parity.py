@@ -31,6 +31,7 @@ from synthetic import make_workload  # noqa: E402
 from synthetic.workloads import custom  # noqa: E402
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+BAL = pa.PA_PARTITION_BALANCED
 
 
 def say(*a):
@@ -89,7 +90,7 @@ def test_cache_and_decode_match_oracle(label, name, kw):
     kb, vb = pool.bits()
     assert np.array_equal(host_bits(kl), kb), "key pool differs"
     assert np.array_equal(host_bits(vl), vb), "value pool differs"
-    for ps in sorted({0, w.partition_size, 32, 64, 512}):
+    for ps in sorted({0, w.partition_size, 32, 64, 512, BAL}):
         say(label, "partition", ps)
         out = dev.attend(partition_size=ps)
         torch.cuda.synchronize()
@@ -120,7 +121,7 @@ def test_edge_shapes(case):
     pool, ref = oracle_for(w)
     dev = build_device_batch(w)
     dev.cache_append()
-    for ps in (0, 32, 64):
+    for ps in (0, 32, 64, BAL):
         out = out_f64(dev.attend(partition_size=ps))
         torch.cuda.synchronize()
         for b, L in enumerate(lens):
@@ -145,10 +146,10 @@ def test_block_placement_is_bitwise_invisible():
             w.free_order = w.free_order[::-1].copy()
         dev = build_device_batch(w)
         dev.cache_append()
-        for ps in (0, 512):
+        for ps in (0, 512, BAL):
             outs.append((order, ps, host_bits(dev.attend(partition_size=ps))))
     torch.cuda.synchronize()
-    for ps in (0, 512):
+    for ps in (0, 512, BAL):
         ref = [o for o in outs if o[1] == ps]
         for o in ref[1:]:
             assert np.array_equal(o[2], ref[0][2]), f"placement {o[0]} changed the result (ps={ps})"
@@ -175,7 +176,7 @@ def test_invalid_device_data_gives_nan_rows_without_fault():
     tables[2, 0] = -1
     lens = dev.seq_lens.clone()
     lens[0] = tables.shape[1] * 16 + 1  # longer than its table row
-    for ps in (0, 32):
+    for ps in (0, 32, BAL):
         out = pa.decode(dev.q, dev.k_cache, dev.v_cache, tables, lens, w.num_kv_heads, w.scale, partition_size=ps)
         o = out_f64(out)
         assert np.isnan(o).all(), "every row of this batch is invalid"
@@ -193,3 +194,46 @@ def test_out_of_pool_slots_are_skipped():
     torch.cuda.synchronize()
     after_k, after_v = (host_bits(x) for x in pa.logical_view(dev.k_cache, dev.v_cache))
     assert np.array_equal(before_k, after_k) and np.array_equal(before_v, after_v)
+
+
+def test_balanced_split_reuses_its_workspace_and_mixes_with_other_modes():
+    """The balanced split's counters return to zero after every call."""
+    w = custom(seed=9, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+               lens=[3000, 1, 0, 700, 2048, 31])
+    pool, ref = oracle_for(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    need = max(pa.decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                         dev.max_blocks, ps) for ps in (BAL, 32))
+    ws = pa.new_workspace(need)
+    outs = []
+    for ps in (BAL, 32, BAL, BAL, 0, BAL):
+        out = pa.decode(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens, w.num_kv_heads, w.scale,
+                        partition_size=ps, workspace=ws)
+        outs.append((ps, host_bits(out)))
+        check_out(out_f64(out), ref, w.dtype, what=f"reuse ps={ps}")
+    torch.cuda.synchronize()
+    cnt = pa.lib().pa_decode_counter_bytes(w.batch, w.num_kv_heads)
+    assert int(ws[:cnt].count_nonzero()) == 0, "counters not back to zero"
+    bal = [o for ps, o in outs if ps == BAL]
+    for o in bal[1:]:
+        assert np.array_equal(o, bal[0]), "balanced split is not deterministic"
+
+
+def test_balanced_split_many_sequences():
+    """More sequences than one wave's lanes (several prefix-scan chunks), with empty ones mixed in."""
+    rng = np.random.default_rng(10)
+    lens = [int(x) for x in rng.integers(0, 90, size=300)]
+    lens[0], lens[150], lens[299] = 0, 0, 1
+    w = custom(seed=10, dtype="bf16", num_q_heads=16, num_kv_heads=2, head_dim=64, block_size=8, lens=lens)
+    say("many sequences", w.batch, "sum L", sum(lens))
+    pool, ref = oracle_for(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    for ps in (BAL, 0):
+        out = out_f64(dev.attend(partition_size=ps))
+        torch.cuda.synchronize()
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.array_equal(out[b], np.zeros_like(out[b]))
+        check_out(out, ref, w.dtype, what=f"many ps={ps}")
