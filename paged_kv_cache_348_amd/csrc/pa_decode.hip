@@ -52,6 +52,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 
 #include "pa.h"
@@ -69,7 +70,7 @@ struct DecodeCfg {
     static constexpr int NT = BF16 ? 2 : 1;             // 16-row key tiles per step
     static constexpr int NKC = BF16 ? D / 32 : D / 16;  // 16-byte key loads per lane per tile
     static constexpr int NV = D / 16;                   // 16-byte value loads per lane per step
-    static constexpr int VT = BF16 ? 8 : 4;             // tokens in one value load
+    static constexpr int VT = 4;                        // tokens in one value load (f32) / half-load (bf16)
     static constexpr int NE = STEP / BS > 0 ? STEP / BS : 1;  // table entries a step touches
     static constexpr int64_t TILE = (int64_t)D * BS;    // elements of one (block, head) tile
     typedef u32x4 QRegs[NKC];                           // query operand of one lane
@@ -82,20 +83,39 @@ struct StepRegs {
     u32x4 v[DecodeCfg<BF16, D, BS>::NV];
 };
 
-// Physical block holding token t of a step starting at tok0, from the
-// step's table entries e[] (entry k covers tokens tok0/BS*BS + k*BS ...).
+// Physical blocks of the (at most four) blocks one step touches, as four
+// scalars (an array here would be turned into a per-lane indexed copy in
+// scratch memory).
+struct StepBlocks {
+    int32_t e0, e1, e2, e3;
+};
+
+// Physical block holding token t of a step starting at tok0 (entry k covers
+// tokens tok0/BS*BS + k*BS ...).  With four entries the lane's entry is
+// fetched with a cross-lane read from lanes 0..3 (a chain of selects on a
+// per-lane index would be turned into an indexed copy in scratch memory).
 template <int NE, int BS>
-__device__ __forceinline__ int32_t pick_block(const int32_t (&e)[NE], int t, int tok0) {
+__device__ __forceinline__ int32_t pick_block(const StepBlocks& e, int t, int tok0) {
     if constexpr (NE == 1) {
-        return e[0];
+        return e.e0;
+    } else if constexpr (NE == 2) {
+        return (t / BS - tok0 / BS == 1) ? e.e1 : e.e0;
     } else {
-        const int k = t / BS - tok0 / BS;
-        int32_t r = e[0];
-#pragma unroll
-        for (int i = 1; i < NE; ++i) r = (k == i) ? e[i] : r;
-        return r;
+        const int lane = threadIdx.x & 63;
+        int32_t ev = e.e0;
+        ev = (lane == 1) ? e.e1 : ev;
+        ev = (lane == 2) ? e.e2 : ev;
+        ev = (lane == 3) ? e.e3 : ev;
+        return __shfl(ev, t / BS - tok0 / BS, 64);
     }
 }
+
+// Issue the loads of one step (tokens tok0 .. tok0 + STEP - 1, clamped to
+// L - 1) given the physical blocks e[] of the step's blocks.
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void issue_step_e(StepRegs<BF16, D, BS>& r, const char* __restrict__ kbase,
+                                             const char* __restrict__ vbase, int64_t blk_bytes, const StepBlocks& e,
+                                             int tok0, int L, int n, int j);
 
 template <bool BF16, int D, int BS>
 __device__ __forceinline__ void issue_step(StepRegs<BF16, D, BS>& r, const char* __restrict__ kbase,
@@ -103,19 +123,26 @@ __device__ __forceinline__ void issue_step(StepRegs<BF16, D, BS>& r, const char*
                                            int32_t ent, int blk0, int nblk, int tok0, int L, int n, int j) {
     using C = DecodeCfg<BF16, D, BS>;
     // table entries of the blocks this step touches (wave-uniform)
-    int32_t e[C::NE];
     const int rel0 = tok0 / BS - blk0;
-#pragma unroll
-    for (int i = 0; i < C::NE; ++i) {
-        const int rel = min(rel0 + i, nblk - 1);
-        e[i] = lane_value(ent, rel);
-    }
+    StepBlocks e;
+    e.e0 = lane_value(ent, rel0);
+    e.e1 = C::NE > 1 ? lane_value(ent, min(rel0 + 1, nblk - 1)) : 0;
+    e.e2 = C::NE > 2 ? lane_value(ent, min(rel0 + 2, nblk - 1)) : 0;
+    e.e3 = C::NE > 3 ? lane_value(ent, min(rel0 + 3, nblk - 1)) : 0;
+    issue_step_e<BF16, D, BS>(r, kbase, vbase, blk_bytes, e, tok0, L, n, j);
+}
+
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void issue_step_e(StepRegs<BF16, D, BS>& r, const char* __restrict__ kbase,
+                                             const char* __restrict__ vbase, int64_t blk_bytes, const StepBlocks& e,
+                                             int tok0, int L, int n, int j) {
+    using C = DecodeCfg<BF16, D, BS>;
     const int last = L - 1;
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
-        // key row n of tile t holds token: bf16 tile a 8*(n/4)+n%4, tile b +4; f32 token n
-        int tok = BF16 ? tok0 + 8 * (n >> 2) + (n & 3) + 4 * t : tok0 + n;
-        tok = min(tok, last);  // rows past the end read a valid slot and are masked later
+        // key row n of tile t is token tok0 + 16 t + n: for a fixed lane group
+        // the 16 rows are 256 contiguous bytes of one chunk column
+        const int tok = min(tok0 + 16 * t + n, last);  // rows past the end read a valid slot, masked later
         const int32_t phys = pick_block<C::NE, BS>(e, tok, tok0);
         const char* kp = kbase + (int64_t)phys * blk_bytes + (int64_t)(tok % BS) * 16;
 #pragma unroll
@@ -124,30 +151,60 @@ __device__ __forceinline__ void issue_step(StepRegs<BF16, D, BS>& r, const char*
             r.k[t][c] = ld16_stream(kp + (int64_t)chunk * BS * 16);
         }
     }
-    // values: lane group j reads tokens [tok0 + VT*j, +VT) of head-dim row d
-    int tv = tok0 + C::VT * j;
-    tv = min(tv, last & ~(C::VT - 1));
-    const int32_t pv = pick_block<C::NE, BS>(e, tv, tok0);
-    const char* vp = vbase + (int64_t)pv * blk_bytes + (int64_t)(tv % BS) * C::ES;
+    if constexpr (BF16) {
+        // values: lane group j reads tokens tok0 + 4j .. +3 (tile 0) and
+        // tok0 + 16 + 4j .. +3 (tile 1) of head-dim row d, the tokens whose
+        // scores it holds; one 8-byte load each
+        const int ta = min(tok0 + 4 * j, last & ~3);
+        const int tb = min(tok0 + 16 + 4 * j, last & ~3);
+        const char* va = vbase + (int64_t)pick_block<C::NE, BS>(e, ta, tok0) * blk_bytes + (int64_t)(ta % BS) * 2;
+        const char* vb = vbase + (int64_t)pick_block<C::NE, BS>(e, tb, tok0) * blk_bytes + (int64_t)(tb % BS) * 2;
 #pragma unroll
-    for (int c = 0; c < C::NV; ++c) {
-        const int d = 16 * c + n;
-        r.v[c] = ld16_stream(vp + (int64_t)d * BS * C::ES);
+        for (int c = 0; c < C::NV; ++c) {
+            const int64_t d = 16 * c + n;
+            const u32x2 lo = ld8_stream(va + d * BS * 2);
+            const u32x2 hi = ld8_stream(vb + d * BS * 2);
+            r.v[c] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    } else {
+        // values: lane group j reads tokens [tok0 + 4j, +4) of head-dim row d
+        int tv = tok0 + C::VT * j;
+        tv = min(tv, last & ~(C::VT - 1));
+        const int32_t pv = pick_block<C::NE, BS>(e, tv, tok0);
+        const char* vp = vbase + (int64_t)pv * blk_bytes + (int64_t)(tv % BS) * C::ES;
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) {
+            const int d = 16 * c + n;
+            r.v[c] = ld16_stream(vp + (int64_t)d * BS * C::ES);
+        }
     }
 }
 
-__device__ __forceinline__ float wave_max16(float x) {
-    // reduce over the four lanes l, l^16, l^32, l^48 (the same head column)
-    x = fmaxf(x, shfl_xor_f(x, 16));
-    x = fmaxf(x, shfl_xor_f(x, 32));
-    return x;
+// Reductions over the four lanes l, l^16, l^32, l^48 (one head column).
+// gfx950's permlane swaps exchange 16-lane rows (and 32-lane halves)
+// between two registers in the vector ALU, so no LDS crossbar operation
+// (and no wait shared with scalar loads) is involved: after a swap of a
+// value with itself, the two results hold x[l] and x[l ^ 16] (or x[l ^ 32])
+// in every lane, in the same order in both partner lanes.
+__device__ __forceinline__ float pair16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float wave_sum16(float x) {
-    x += shfl_xor_f(x, 16);
-    x += shfl_xor_f(x, 32);
-    return x;
-}
+__device__ __forceinline__ float wave_max16(float x) { return pair32_max(pair16_max(x)); }
+__device__ __forceinline__ float wave_sum16(float x) { return pair32_sum(pair16_sum(x)); }
 
 // One loop step: scores of the step's tokens for the G query heads, the
 // online-softmax update and the PV accumulation.  Tokens at or past L are
@@ -161,7 +218,7 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
     using C = DecodeCfg<BF16, D, BS>;
     const bool tail = tok0 + C::STEP > L;
     if constexpr (BF16) {
-        // ---- scores: two 16-token tiles, rows 4j+i <-> tokens 8j+i (tile a), 8j+4+i (tile b)
+        // ---- scores: two 16-token tiles; lane (n, j) receives tokens 4j+i (tile a) and 16+4j+i (tile b)
         f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < C::NKC; ++c) {
@@ -178,13 +235,15 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
             s[4 + i] = sb[i] * scale_log2;
         }
         if (tail) {
-            const int base = tok0 + 8 * j;
+            // element e of the lane's scores / value operand is token tok(e)
+            const int base = tok0 + 4 * j;
+            auto tok = [&](int e) { return base + (e & 3) + ((e >> 2) << 4); };
             uint32_t keep[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] = (base + e < L) ? s[e] : -INFINITY;
+            for (int e = 0; e < 8; ++e) s[e] = (tok(e) < L) ? s[e] : -INFINITY;
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                keep[w] = ((base + 2 * w < L) ? 0x0000ffffu : 0u) | ((base + 2 * w + 1 < L) ? 0xffff0000u : 0u);
+                keep[w] = ((tok(2 * w) < L) ? 0x0000ffffu : 0u) | ((tok(2 * w + 1) < L) ? 0xffff0000u : 0u);
             // values of masked tokens may be NaN: zero them (p = 0 would not)
 #pragma unroll
             for (int c = 0; c < C::NV; ++c)
@@ -323,6 +382,7 @@ __device__ __forceinline__ void attend_range(RunState<BF16, D, BS>& S,
         for (int st = 0; st + 1 < nst; ++st, tok0 += C::STEP) {
             StepRegs<BF16, D, BS> nxt;
             issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, L, n, j);
+            __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the compute
             compute_step<BF16, D, BS>(cur, qr, S.m, S.l, S.acc, tok0, L, j, scale_log2);
             cur = nxt;
         }
@@ -502,24 +562,286 @@ __device__ __forceinline__ float2 coherent_load(const uint64_t* p) {
     return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
+// Wave-uniform copies (values read from LDS land in vector registers; the
+// loop state derived from them is kept in scalar registers this way).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Wave (of nw) whose step range holds global step x; wave w covers
 // [S*w/nw, S*(w+1)/nw).
 __device__ __forceinline__ int wave_of_step(int64_t x, int64_t S, int nw) {
     return (int)(((x + 1) * nw - 1) / S);
 }
 
+// A wave's position in the global step order (all fields wave-uniform).
+struct StepCursor {
+    int b;    // sequence
+    int g;    // kv-head
+    int ls;   // step within the (sequence, kv-head) segment
+    int nst;  // steps of that segment
+    int L;    // length of sequence b
+};
+
+// Advance one step, skipping sequences without steps.  Called only while
+// a next step exists, so a later sequence with steps exists too.
+__device__ __forceinline__ void cursor_next(StepCursor& c, const int32_t* s_steps, const int32_t* s_len, int Hkv) {
+    if (++c.ls < c.nst) return;
+    c.ls = 0;
+    if (++c.g < Hkv) return;
+    c.g = 0;
+    do {
+        ++c.b;
+    } while (uniform(s_steps[c.b]) == 0);
+    c.nst = uniform(s_steps[c.b]);
+    c.L = uniform(s_len[c.b]);
+}
+
+// What the load stage of a step needs: its sequence length and the
+// physical blocks of its tokens.  The table entries are read with scalar
+// loads (wave-uniform addresses); their wait counter is shared only with
+// the rare LDS reads of the step cursor.  An entry outside the pool is
+// replaced by block 0 (so no load leaves the pool) and flags the step.
+struct StepInfo {
+    StepBlocks e;
+    int L;
+    bool bad;
+};
+
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void fetch_step(StepInfo& f, const StepCursor& c, const int32_t* __restrict__ tables,
+                                           int max_blocks, int num_blocks) {
+    using C = DecodeCfg<BF16, D, BS>;
+    const int32_t* trow = tables + (int64_t)c.b * max_blocks;
+    const int blk = c.ls * C::STEP / BS;
+    const int lastb = (c.L - 1) / BS;
+    bool bad = false;
+    auto entry = [&](int i) {
+        const int32_t v = trow[min(blk + i, lastb)];
+        const bool ok = v >= 0 && v < num_blocks;
+        bad |= !ok;
+        return ok ? v : 0;
+    };
+    f.e.e0 = entry(0);
+    f.e.e1 = C::NE > 1 ? entry(1) : 0;
+    f.e.e2 = C::NE > 2 ? entry(2) : 0;
+    f.e.e3 = C::NE > 3 ? entry(3) : 0;
+    f.L = c.L;
+    f.bad = bad;
+}
+
+// Query operand loaded by every lane: the padding columns n >= G repeat
+// head G-1.  Their scores, softmax statistics and outputs stay in their own
+// columns and are never stored, and the loaded registers are used as they
+// arrive (touching them here would make this stage wait for the load).
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void load_q_all(typename DecodeCfg<BF16, D, BS>::QRegs& qr, const void* __restrict__ q_,
+                                           int64_t row0, int n, int j, int G) {
+    using C = DecodeCfg<BF16, D, BS>;
+    const char* qp = reinterpret_cast<const char*>(q_) + (row0 + min(n, G - 1)) * D * C::ES;
+#pragma unroll
+    for (int c = 0; c < C::NKC; ++c) qr[c] = ld16(qp + (int64_t)(4 * c + j) * 16);
+}
+
+// A cut (sequence, kv-head) whose piece this wave left in a partial slot.
+struct CutPiece {
+    bool valid;
+    int b, g;
+    int64_t seg0, seg1;  // the segment's global steps [seg0, seg1)
+};
+
+// Count a piece in; the wave that brings the segment's counter to its
+// piece count merges every piece (log-sum-exp rule), writes the G rows and
+// puts the counter back to zero.
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void count_in(const CutPiece& cp, const float* __restrict__ slot_o,
+                                         const float* __restrict__ slot_ml, int32_t* __restrict__ counters,
+                                         void* __restrict__ out_, int64_t S, int nw, int Hq, int Hkv, int G, int lane,
+                                         int n, int j) {
+    using C = DecodeCfg<BF16, D, BS>;
+    const int w0 = wave_of_step(cp.seg0, S, nw);
+    const int w1 = wave_of_step(cp.seg1 - 1, S, nw);
+    int32_t* cnt = counters + (int64_t)cp.b * Hkv + cp.g;
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    if (old != w1 - w0) return;
+    if (n < G) {
+        float M = -INFINITY;
+        for (int k = w0; k <= w1; ++k) {
+            const int64_t sk = 2 * (int64_t)k + ((k == w0 && cp.seg0 != S * k / nw) ? 1 : 0);
+            M = fmaxf(M, coherent_load(reinterpret_cast<const uint64_t*>(slot_ml + (sk * G + n) * 2)).x);
+        }
+        RunState<BF16, D, BS> Mg;
+        Mg.m = M;
+        Mg.l = 0.0f;
+        Mg.bad = false;
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) Mg.acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k = w0; k <= w1; ++k) {
+            const int64_t sk = 2 * (int64_t)k + ((k == w0 && cp.seg0 != S * k / nw) ? 1 : 0);
+            const float2 ml = coherent_load(reinterpret_cast<const uint64_t*>(slot_ml + (sk * G + n) * 2));
+            const float wt = __builtin_amdgcn_exp2f(ml.x - M);
+            Mg.l += wt * ml.y;
+            const uint64_t* po = reinterpret_cast<const uint64_t*>(slot_o + (sk * G + n) * D);
+#pragma unroll
+            for (int c = 0; c < C::NV; ++c) {
+                const int e = (16 * c + 4 * j) / 2;
+                const float2 lo = coherent_load(po + e), hi = coherent_load(po + e + 1);
+                Mg.acc[c] += wt * f32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+        }
+        store_out<BF16, D, BS>(out_, (int64_t)cp.b * Hq + cp.g * G, Mg, n, j, G);
+    }
+    if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Finish the piece whose last step was just computed: a whole segment is
+// written out; a cut one leaves its partial in slot (w, 0) if it is the
+// wave's first piece, else (w, 1), and is remembered for counting in.
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void finish_piece(const RunState<BF16, D, BS>& St, const StepCursor& cc, bool seg_begin,
+                                             bool& first_piece, CutPiece& cut0, CutPiece& cut1,
+                                             const int64_t* s_first, float* __restrict__ slot_o,
+                                             float* __restrict__ slot_ml, void* __restrict__ out_, int w, int Hq,
+                                             int G, int n, int j) {
+    using C = DecodeCfg<BF16, D, BS>;
+    const bool complete = seg_begin && cc.ls == cc.nst - 1;
+    if (complete) {
+        store_out<BF16, D, BS>(out_, (int64_t)cc.b * Hq + cc.g * G, St, n, j, G);
+    } else {
+        const int64_t slot = 2 * (int64_t)w + (first_piece ? 0 : 1);
+        if (n < G) {
+            uint64_t* po = reinterpret_cast<uint64_t*>(slot_o + (slot * G + n) * D);
+#pragma unroll
+            for (int c = 0; c < C::NV; ++c) {
+                const f32x4 a = St.bad ? f32x4{NAN, NAN, NAN, NAN} : St.acc[c];
+                const int e = (16 * c + 4 * j) / 2;
+                coherent_store(po + e, a[0], a[1]);
+                coherent_store(po + e + 1, a[2], a[3]);
+            }
+            if (j == 0)
+                coherent_store(reinterpret_cast<uint64_t*>(slot_ml + (slot * G + n) * 2), St.bad ? 0.0f : St.m,
+                               St.bad ? 1.0f : St.l);
+        }
+        const int64_t seg0 = uniform64(s_first[cc.b]) + (int64_t)cc.g * cc.nst;
+        const CutPiece cp = {true, cc.b, cc.g, seg0, seg0 + cc.nst};
+        if (first_piece)
+            cut0 = cp;
+        else
+            cut1 = cp;
+    }
+    first_piece = false;
+}
+
+// One wave's state in the balanced kernel and its pipeline stages.  For
+// compute step x an iteration (1) issues the key/value/query loads of step
+// x+1 with the table entries fetched one iteration earlier, (2) fetches the
+// entries of step x+2 with scalar loads and (3) computes step x.  A piece
+// ends where its segment ends or at the wave's last step.
+template <bool BF16, int D, int BS>
+struct BalancedWave {
+    using C = DecodeCfg<BF16, D, BS>;
+    const void* q_;
+    const char* kc;
+    const char* vc;
+    const int32_t* tables;
+    const int64_t* s_first;
+    const int32_t* s_steps;
+    const int32_t* s_len;
+    void* out_;
+    float* slot_o;
+    float* slot_ml;
+    int Hq, Hkv, G, max_blocks, num_blocks;
+    float scale_log2;
+    int w, n, j;
+    int64_t wend;
+    int64_t blk_bytes;
+    StepCursor cc, ci;  // steps x (compute) and x+1 (issue)
+    StepInfo fe;        // fetched table entries of step x+1 (of x+2 after the fetch stage)
+    bool bad_c, bad_i;  // bad table entry in step x / x+1
+    RunState<BF16, D, BS> St;
+    bool seg_begin, first_piece;
+    CutPiece cut0, cut1;
+
+    __device__ __forceinline__ void issue(StepRegs<BF16, D, BS>& buf, typename C::QRegs& q, const StepCursor& c,
+                                          const StepInfo& f) {
+        const int64_t hb = (int64_t)c.g * C::TILE * C::ES;
+        issue_step_e<BF16, D, BS>(buf, kc + hb, vc + hb, blk_bytes, f.e, c.ls * C::STEP, c.L, n, j);
+        load_q_all<BF16, D, BS>(q, q_, (int64_t)c.b * Hq + c.g * G, n, j, G);
+    }
+
+    // step x0 loaded into (buf, q); entries of x0+1 fetched
+    __device__ __forceinline__ void prologue(StepRegs<BF16, D, BS>& buf, typename C::QRegs& q, int64_t x0) {
+        StepInfo f0;
+        fetch_step<BF16, D, BS>(f0, cc, tables, max_blocks, num_blocks);
+        bad_c = f0.bad;
+        issue(buf, q, cc, f0);
+        ci = cc;
+        if (x0 + 1 < wend) {
+            cursor_next(ci, s_steps, s_len, Hkv);
+            fetch_step<BF16, D, BS>(fe, ci, tables, max_blocks, num_blocks);
+        }
+    }
+
+    __device__ __forceinline__ void compute(StepRegs<BF16, D, BS>& buf, const typename C::QRegs& q) {
+        compute_step<BF16, D, BS>(buf, q, St.m, St.l, St.acc, cc.ls * C::STEP, cc.L, j, scale_log2);
+        St.bad |= bad_c;
+    }
+
+    __device__ __forceinline__ void finish() {
+        finish_piece<BF16, D, BS>(St, cc, seg_begin, first_piece, cut0, cut1, s_first, slot_o, slot_ml, out_, w, Hq,
+                                  G, n, j);
+    }
+
+    // one iteration for compute step x (x + 1 < wend): load into (bl, ql), compute (bc, qc)
+    __device__ __forceinline__ void iter(StepRegs<BF16, D, BS>& bl, typename C::QRegs& ql,
+                                         StepRegs<BF16, D, BS>& bc, const typename C::QRegs& qc, int64_t x) {
+        issue(bl, ql, ci, fe);
+        bad_i = fe.bad;
+        StepCursor cf = ci;
+        if (x + 2 < wend) {
+            cursor_next(cf, s_steps, s_len, Hkv);
+            fetch_step<BF16, D, BS>(fe, cf, tables, max_blocks, num_blocks);
+        }
+        // keep the compiler from hoisting the compute (and its wait) above the loads
+        __builtin_amdgcn_sched_barrier(0);
+        compute(bc, qc);
+        if (cc.ls == cc.nst - 1) finish();
+        cc = ci;
+        bad_c = bad_i;
+        ci = cf;
+        if (cc.ls == 0) {
+            run_init(St);
+            seg_begin = true;
+        }
+    }
+
+    // the wave's last step
+    __device__ __forceinline__ void last(StepRegs<BF16, D, BS>& bc, const typename C::QRegs& qc) {
+        compute(bc, qc);
+        finish();
+    }
+};
+
 // Balanced split ("stream-K" over the attention's token steps).
 //
 // The work is the sequence of segments (b, g), b-major, each of
 // ceil(L_b / STEP) steps.  Wave w of nw takes the global steps
 // [S*w/nw, S*(w+1)/nw), so every wave reads the same number of key/value
-// bytes whatever the length mix.  A segment wholly inside one wave is
-// written directly.  A segment cut by wave boundaries leaves one partial
-// (unnormalised accumulator, running maximum and sum) per piece in the
-// workspace; each piece then bumps the segment's counter, and the wave that
-// brings it to the piece count merges the pieces with the log-sum-exp rule,
-// writes the rows and puts the counter back to zero.  No wave waits for
-// another.
+// bytes whatever the length mix.  The wave runs one three-stage pipeline
+// over all its steps, across segment boundaries: at step x it reads the
+// table entries of step x+2, issues the key/value/query loads of step x+1
+// and computes step x, so a new segment costs no extra memory round trip.
+// A segment wholly inside the wave is written directly.  A segment cut by
+// a wave boundary leaves one partial (unnormalised accumulator, running
+// maximum and sum) per piece in the workspace; after its loop each wave
+// counts its cut pieces in, and the wave that completes a segment's count
+// merges its pieces, writes the rows and puts the counter back to zero.
+// No wave waits for another.
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(
     const void* __restrict__ q_, const void* __restrict__ kc_, const void* __restrict__ vc_,
@@ -529,6 +851,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     using C = DecodeCfg<BF16, D, BS>;
     __shared__ int64_t s_first[kBalancedMaxSeqs];  // global step where sequence b's segments start
     __shared__ int32_t s_steps[kBalancedMaxSeqs];  // steps per segment of sequence b (0: no work)
+    __shared__ int32_t s_len[kBalancedMaxSeqs];    // length of sequence b
     const int lane = threadIdx.x;
     const int n = lane & 15;
     const int j = lane >> 4;
@@ -556,9 +879,11 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
         if (b < B) {
             s_first[b] = S + incl - v;
             s_steps[b] = st;
+            s_len[b] = L;
         }
         S += __shfl(incl, 63, 64);
     }
+    S = uniform64(S);
     __syncthreads();
 
     // 2. rows no segment covers: empty sequences (zeros) and lengths the
@@ -574,103 +899,75 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     const int64_t wbeg = S * w / nw;
     const int64_t wend = S * (w + 1) / nw;
 
-    // 3. the sequence holding step wbeg: the last b with s_first[b] <= wbeg
+    // 3. cursor at step wbeg: the last b with s_first[b] <= wbeg holds it
     int lo = 0, hi = B - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_first[mid] <= wbeg) lo = mid;
+        if (uniform64(s_first[mid]) <= wbeg) lo = mid;
         else hi = mid - 1;
     }
-    int b = lo;
+    StepCursor cc;
+    cc.b = uniform(lo);
+    cc.nst = uniform(s_steps[cc.b]);
+    cc.L = uniform(s_len[cc.b]);
+    {
+        const int64_t off = wbeg - uniform64(s_first[cc.b]);
+        cc.g = (int)(off / cc.nst);
+        cc.ls = (int)(off % cc.nst);
+    }
 
-    const int64_t blk_bytes = (int64_t)Hkv * C::TILE * C::ES;
-    int64_t pos = wbeg;
-    while (pos < wend) {
-        while (pos >= s_first[b] + (int64_t)s_steps[b] * Hkv) ++b;  // skip finished / empty sequences
-        const int nst = s_steps[b];
-        const int g = (int)((pos - s_first[b]) / nst);
-        const int64_t seg0 = s_first[b] + (int64_t)g * nst;
-        const int64_t seg1 = seg0 + nst;
-        const int64_t pend = min(seg1, wend);
-        const int L = lens[b];
-        const int t0 = (int)(pos - seg0) * C::STEP;
-        const int t1 = min((int)(pend - seg0) * C::STEP, L);
-        const int64_t row0 = (int64_t)b * Hq + g * G;
+    // 4. the pipeline: stage buffers A and B alternate, so no loaded
+    //    register is ever copied (a copy would have to wait for its load)
+    BalancedWave<BF16, D, BS> W;
+    W.q_ = q_;
+    W.kc = reinterpret_cast<const char*>(kc_);
+    W.vc = reinterpret_cast<const char*>(vc_);
+    W.tables = tables;
+    W.s_first = s_first;
+    W.s_steps = s_steps;
+    W.s_len = s_len;
+    W.out_ = out_;
+    W.slot_o = slot_o;
+    W.slot_ml = slot_ml;
+    W.Hq = Hq;
+    W.Hkv = Hkv;
+    W.G = G;
+    W.max_blocks = max_blocks;
+    W.num_blocks = num_blocks;
+    W.scale_log2 = scale_log2;
+    W.w = w;
+    W.n = n;
+    W.j = j;
+    W.wend = wend;
+    W.blk_bytes = (int64_t)Hkv * C::TILE * C::ES;
+    W.cc = cc;
+    W.seg_begin = cc.ls == 0;
+    W.first_piece = true;
+    W.cut0 = CutPiece{false, 0, 0, 0, 0};
+    W.cut1 = CutPiece{false, 0, 0, 0, 0};
+    run_init(W.St);
 
-        u32x4 qr[C::NKC];
-        load_q<BF16, D, BS>(qr, q_, row0 + n, n, j, G);
-        RunState<BF16, D, BS> St;
-        run_init(St);
-        attend_range<BF16, D, BS>(St, qr, reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES,
-                                  reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES, blk_bytes,
-                                  tables + (int64_t)b * max_blocks, num_blocks, t0, t1, L, lane, n, j, scale_log2);
+    StepRegs<BF16, D, BS> bufA, bufB;
+    typename C::QRegs qA, qB;
+    W.prologue(bufA, qA, wbeg);
+    int64_t x = wbeg;
+    for (; x + 2 < wend; x += 2) {
+        W.iter(bufB, qB, bufA, qA, x);
+        W.iter(bufA, qA, bufB, qB, x + 1);
+    }
+    if (x + 1 < wend) {
+        W.iter(bufB, qB, bufA, qA, x);
+        W.last(bufB, qB);
+    } else {
+        W.last(bufA, qA);
+    }
+    const CutPiece cut0 = W.cut0, cut1 = W.cut1;
 
-        if (pos == seg0 && pend == seg1) {
-            store_out<BF16, D, BS>(out_, row0, St, n, j, G);
-        } else {
-            // partial of this piece: slot (w, 0) if it holds the wave's first step, else (w, 1).
-            // Partials and the counter are read and written with agent-scope atomic
-            // accesses, which go to the device-coherent level and bypass each XCD's L2,
-            // so no cache-wide write-back or invalidate is needed.
-            const int64_t slot = 2 * (int64_t)w + (pos == wbeg ? 0 : 1);
-            if (n < G) {
-                uint64_t* po = reinterpret_cast<uint64_t*>(slot_o + (slot * G + n) * D);
-#pragma unroll
-                for (int c = 0; c < C::NV; ++c) {
-                    const f32x4 a = St.bad ? f32x4{NAN, NAN, NAN, NAN} : St.acc[c];
-                    const int e = (16 * c + 4 * j) / 2;
-                    coherent_store(po + e, a[0], a[1]);
-                    coherent_store(po + e + 1, a[2], a[3]);
-                }
-                if (j == 0)
-                    coherent_store(reinterpret_cast<uint64_t*>(slot_ml + (slot * G + n) * 2), St.bad ? 0.0f : St.m,
-                                   St.bad ? 1.0f : St.l);
-            }
-            const int w0 = wave_of_step(seg0, S, nw);
-            const int w1 = wave_of_step(seg1 - 1, S, nw);
-            int32_t* cnt = counters + (int64_t)b * Hkv + g;
-            // the partial must be complete at the coherent level before counting in
-            __builtin_amdgcn_s_waitcnt(0);
-            int old = 0;
-            if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            old = __shfl(old, 0, 64);
-            if (old == w1 - w0) {
-                // last piece in: merge every piece of the segment
-                if (n < G) {
-                    float M = -INFINITY;
-                    for (int k = w0; k <= w1; ++k) {
-                        const int64_t sk = 2 * (int64_t)k + ((k == w0 && seg0 != S * k / nw) ? 1 : 0);
-                        M = fmaxf(M, coherent_load(reinterpret_cast<uint64_t*>(slot_ml + (sk * G + n) * 2)).x);
-                    }
-                    float den = 0.0f;
-                    f32x4 num[C::NV];
-#pragma unroll
-                    for (int c = 0; c < C::NV; ++c) num[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    for (int k = w0; k <= w1; ++k) {
-                        const int64_t sk = 2 * (int64_t)k + ((k == w0 && seg0 != S * k / nw) ? 1 : 0);
-                        const float2 ml = coherent_load(reinterpret_cast<uint64_t*>(slot_ml + (sk * G + n) * 2));
-                        const float wt = __builtin_amdgcn_exp2f(ml.x - M);
-                        den += wt * ml.y;
-                        uint64_t* po = reinterpret_cast<uint64_t*>(slot_o + (sk * G + n) * D);
-#pragma unroll
-                        for (int c = 0; c < C::NV; ++c) {
-                            const int e = (16 * c + 4 * j) / 2;
-                            const float2 lo = coherent_load(po + e), hi = coherent_load(po + e + 1);
-                            num[c] += wt * f32x4{lo.x, lo.y, hi.x, hi.y};
-                        }
-                    }
-                    RunState<BF16, D, BS> Mg;
-                    Mg.m = M;
-                    Mg.l = den;
-                    Mg.bad = false;
-#pragma unroll
-                    for (int c = 0; c < C::NV; ++c) Mg.acc[c] = num[c];
-                    store_out<BF16, D, BS>(out_, row0, Mg, n, j, G);
-                }
-                if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        pos = pend;
+    // 5. count the cut pieces in (their partials must be at the coherent level first)
+    if (cut0.valid || cut1.valid) {
+        __builtin_amdgcn_s_waitcnt(0);
+        if (cut0.valid) count_in<BF16, D, BS>(cut0, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
+        if (cut1.valid) count_in<BF16, D, BS>(cut1, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
     }
 }
 
@@ -716,7 +1013,8 @@ int balanced_waves() {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        cached[dev] = std::min(pa::kBalancedMaxWaves, kWavesPerCU * cus);
+        const int wpc = getenv("PA_BAL_WPC") ? atoi(getenv("PA_BAL_WPC")) : kWavesPerCU;
+        cached[dev] = std::min(pa::kBalancedMaxWaves, wpc * cus);
     }
     return cached[dev];
 }

@@ -9,6 +9,7 @@ namespace pa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte global load / store (one global_load_dwordx4 / global_store_dwordx4).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -18,6 +19,11 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 // K/V pool during decode), so it does not displace reusable lines.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// 8-byte streaming load (same policy).
+__device__ __forceinline__ u32x2 ld8_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
 // float -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN).
