@@ -52,7 +52,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 #include <cstdint>
 
 #include "pa.h"
@@ -1013,8 +1012,7 @@ int balanced_waves() {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        const int wpc = getenv("PA_BAL_WPC") ? atoi(getenv("PA_BAL_WPC")) : kWavesPerCU;
-        cached[dev] = std::min(pa::kBalancedMaxWaves, wpc * cus);
+        cached[dev] = std::min(pa::kBalancedMaxWaves, kWavesPerCU * cus);
     }
     return cached[dev];
 }
