@@ -37,6 +37,8 @@ from synthetic import make_workload  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 PARTITION_BALANCED = -1  # the library's balanced split (PA_PARTITION_BALANCED)
+# launch configuration per workload (the long-context ones use their own
+# 512-token partitions with the log-sum-exp merge)
 DEFAULT_PARTITION = {"llama3_8b": PARTITION_BALANCED, "llama_70b": PARTITION_BALANCED,
                      "prefix_share": PARTITION_BALANCED}
 WORKLOAD_TEXT = {

@@ -1,0 +1,76 @@
+"""GPU parity at the full benchmark sizes, on sampled outputs.
+
+Each workload is built at its full size (the lengths, pool and placement the
+benchmark times) and decoded in the launch configuration the benchmark uses.
+The oracle cannot replay pools of several GB in a test's time, so sampled
+sequences are checked one by one: their output rows against the float64
+oracle attention over the same tokens' keys and values (the pages' result is
+exactly plain attention over the sequence in order, so the reference needs
+only the logical K/V the generator hands out), and the decode-step token's
+cache slot against that token's key/value bits.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_348_amd as pa  # noqa: E402
+from paged_kv_cache_348_amd.workload import build_device_batch  # noqa: E402
+import oracle.attention as oa  # noqa: E402
+from synthetic import make_workload  # noqa: E402
+
+TOL = 2e-2  # bf16 keys/values, float32 accumulation
+BAL = pa.PA_PARTITION_BALANCED
+
+# (workload, partition mode the benchmark uses, sequences to sample)
+CASES = [
+    ("llama3_8b", BAL, 6),
+    ("llama_70b", BAL, 4),
+    ("prefix_share", BAL, 6),
+    ("long_ctx_bs8", 512, 2),
+    ("long_ctx_bs16", 512, 2),
+    ("long_ctx_bs32", 512, 2),
+]
+
+
+def say(*a):
+    print("[gpu-full]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t):
+    return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,ps,nsample", CASES, ids=[c[0] for c in CASES])
+def test_full_size_sampled_rows(name, ps, nsample):
+    w = make_workload(name, seed=0)
+    say(name, "B", w.batch, "sum L", int(w.seq_lens.sum()), "NB", w.num_blocks, "partition", ps)
+    dev = build_device_batch(w, partition_size=ps)
+    dev.cache_append()
+    out = dev.attend()
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite output"
+    rng = np.random.default_rng(1234)
+    rows = sorted({int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))}
+                  | set(int(x) for x in rng.choice(w.batch, size=nsample, replace=False)))
+    assert len(dev.host_dec_slots) == w.batch  # every sequence has a decode token here
+    for b in rows:
+        K, V = w.sequence_kv(b)
+        ref = oa.dense_attention(oa.widen(w.q[b]), oa.widen(K), oa.widen(V), w.scale)
+        err = float(np.abs(got[b] - ref).max())
+        say(name, "row", b, "L", int(w.seq_lens[b]), "max abs err", f"{err:.3e}")
+        assert err <= TOL, (name, b, err)
+        # the decode token of sequence b sits in its slot, bit for bit
+        blk, off = divmod(int(dev.host_dec_slots[b]), w.block_size)
+        key = dev.k_cache[blk, :, :, off, :].reshape(w.num_kv_heads, w.head_dim)
+        val = dev.v_cache[blk, :, :, off]
+        assert np.array_equal(bits(key), K[-1]), "decode-token key not in its slot"
+        assert np.array_equal(bits(val), V[-1]), "decode-token value not in its slot"
+    w.drop_kv()
