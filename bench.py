@@ -61,6 +61,29 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary of this
+    workload (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by their
+    calibrations), or None when there is none or the decode sources changed
+    since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    h = hashlib.sha256()
+    for f in ("pa_decode.hip", "pa_device.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_348_amd", "csrc", f), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 # ---------------------------------------------------------------------------- CPU baseline (the oracle)
 
 _CPU = {}
@@ -164,14 +187,25 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
     ms_step = ev0.elapsed_time(ev1) / steps
     out = dev.out.float().cpu().numpy().astype(np.float64)
 
-    # decode kernel alone: one event pair per launch, hot and with L2/MALL flushed
-    # (the flush reads 1 GiB, so it leaves no dirty lines to write back later)
-    def time_decode(n, flush):
-        scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda") if flush else None
+    # decode alone.  Hot: `n` launches back to back between one event pair
+    # (per-launch events would add their own gaps).  Cold: one event pair per
+    # launch, each after a 1 GiB read that evicts L2 and MALL (a read leaves
+    # no dirty lines to write back during the timed launch).
+    def time_decode_hot(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(n):
+            dev.attend()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    def time_decode_cold(n):
+        scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         for a, b in evs:
-            if flush:
-                scratch.amax()
+            scratch.amax()
             a.record(stream)
             dev.attend()
             b.record(stream)
@@ -180,8 +214,8 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
         del scratch
         return t
 
-    hot = time_decode(max(steps, 20), False)
-    cold = time_decode(cold_iters, True)
+    hot = np.array([time_decode_hot(max(steps, 20)) for _ in range(3)])
+    cold = time_decode_cold(cold_iters)
 
     # calibration: a plain streaming read of the same byte count
     import paged_kv_cache_348_amd as pa
@@ -256,7 +290,7 @@ def main(argv=None):
     g = gpu_bench(w, args.steps, args.warmup, ps)
     ms = g["ms_step"]
     hot, cold = g["hot_ms"], g["cold_ms"]
-    t_dec = float(hot.mean()) * 1e-3
+    t_dec = float(np.median(hot)) * 1e-3
     achieved = kv_bytes / t_dec / 1e9
     err = None
     if ref is not None:
@@ -293,7 +327,7 @@ def main(argv=None):
         },
         "kv_read_gbps_step": kv_bytes / (ms * 1e-3) / 1e9,
         "kv_read_frac_of_8tbs_step": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "decode_us": {"hot_mean": float(hot.mean()) * 1e3, "hot_min": float(hot.min()) * 1e3,
+        "decode_us": {"hot": float(np.median(hot)) * 1e3, "hot_runs": [float(x) * 1e3 for x in hot],
                       "cold_median": float(np.median(cold)) * 1e3, "cold_min": float(cold.min()) * 1e3},
         "cache_append_us": g["ms_append"] * 1e3,
         "stream_read_gbps_same_bytes": g["stream_read_gbps"],
@@ -305,7 +339,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(args.workload) if ps == DEFAULT_PARTITION.get(args.workload, ps) else None,
             "algorithmic_bytes_per_launch": kv_bytes,
             "flop_per_launch": flop,
         },
