@@ -41,10 +41,13 @@
  * X = 16 / sizeof(element) (8 for bf16, 4 for f32) and head_dim % X == 0:
  *    k_cache: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
  *    v_cache: [num_blocks][num_kv_heads][head_dim][block_size]
- * The key of the token in slot s (block s / bs, offset s % bs), kv-head h,
- * dimension d is k_cache[s/bs][h][d/X][s%bs][d%X]; its value is
- * v_cache[s/bs][h][d][s%bs].  A (block, head) tile is contiguous
- * (block_size * head_dim elements for each of K and V).
+ * The key of the token in slot s (block s / bs, offset o = s % bs), kv-head
+ * h, dimension d is k_cache[s/bs][h][d/X][o][d%X]; its value is
+ * v_cache[s/bs][h][d][vpos(o)], where vpos(o) = o for f32 and for bf16 with
+ * block_size 8, and for bf16 with block_size 16 or 32 vpos swaps bits 2 and
+ * 3 of o (0-3, 8-11, 4-7, 12-15 within each 16 offsets): the 8 values a
+ * matrix-core lane needs are then one 16-byte load.  A (block, head) tile is
+ * contiguous (block_size * head_dim elements for each of K and V).
  */
 #ifndef PA_H
 #define PA_H

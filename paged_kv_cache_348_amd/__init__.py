@@ -9,8 +9,10 @@ and streams.
 Device cache layout (per layer), X = 16 bytes / element size:
     k_cache [num_blocks, num_kv_heads, head_dim // X, block_size, X]
     v_cache [num_blocks, num_kv_heads, head_dim, block_size]
-``logical_view`` presents both as [num_blocks, num_kv_heads, block_size,
-head_dim], the pages' per-layer layout.
+where a bfloat16 value of in-block offset o with block_size 16 or 32 sits
+at ``value_position(o)`` (bits 2 and 3 of o swapped).  ``logical_view``
+presents both as [num_blocks, num_kv_heads, block_size, head_dim], the
+pages' per-layer layout.
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ from ._lib import (PA_BF16, PA_PARTITION_BALANCED, PA_ERR_EXISTS, PA_ERR_INVALID
 
 __all__ = [
     "PAError", "Allocator", "cache_write", "copy_blocks", "decode", "decode_workspace_bytes", "new_kv_cache",
-    "kv_cache_shapes", "logical_view", "stream_read", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_OOM",
+    "kv_cache_shapes", "logical_view", "value_position", "stream_read", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_OOM",
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
     "new_workspace",
 ]
@@ -99,10 +101,20 @@ def _pool_dims(k_cache, v_cache):
     return nb, hkv, bs, d
 
 
+def value_position(offset: int, block_size: int, dtype) -> int:
+    """Position along v_cache's last axis of the value with in-block offset ``offset``."""
+    if _dtype_code(dtype) == PA_BF16 and block_size >= 16:
+        return (offset & ~12) | ((offset & 4) << 1) | ((offset & 8) >> 1)
+    return offset
+
+
 def logical_view(k_cache, v_cache):
-    """Both caches as [NB, Hkv, bs, D] (the keys are gathered into a new tensor, the values are a view)."""
+    """Both caches as [NB, Hkv, bs, D] (new tensors gathered from the device layout)."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
-    return k_cache.permute(0, 1, 3, 2, 4).reshape(nb, hkv, bs, d), v_cache.transpose(2, 3)
+    perm = [value_position(o, bs, v_cache.dtype) for o in range(bs)]
+    idx = _torch().tensor(perm, device=v_cache.device)
+    return (k_cache.permute(0, 1, 3, 2, 4).reshape(nb, hkv, bs, d),
+            v_cache.index_select(3, idx).transpose(2, 3).contiguous())
 
 
 def cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:

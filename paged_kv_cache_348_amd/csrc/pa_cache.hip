@@ -7,7 +7,9 @@
 // comparison table, "Copy on write blocks").
 //
 // Pool tile layout (include/pa.h): keys [head_dim/X][block_size][X], values
-// [head_dim][block_size] per (block, kv-head), X = 16 bytes of elements.
+// [head_dim][block_size] per (block, kv-head), X = 16 bytes of elements; bf16
+// values in blocks of 16 or 32 tokens sit at the in-block offset with bits 2
+// and 3 swapped.
 // One thread moves one 16-byte chunk of a token's key (a 16-byte store) and
 // the same chunk of its value (X element stores, block_size apart).
 
@@ -40,7 +42,10 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict
     st16(kc + (tile + ((int64_t)c * BS + off) * X) * ES, ld16(k + src));
     const u32x4 vv = ld16(v + src);
     if constexpr (ES == 2) {
-        uint16_t* vt = reinterpret_cast<uint16_t*>(vc) + tile + (int64_t)c * X * BS + off;
+        // bf16 blocks of 16 or 32 tokens store values with bits 2 and 3 of the
+        // in-block offset swapped (include/pa.h)
+        const int vpos = BS >= 16 ? (off & ~12) | ((off & 4) << 1) | ((off & 8) >> 1) : off;
+        uint16_t* vt = reinterpret_cast<uint16_t*>(vc) + tile + (int64_t)c * X * BS + vpos;
 #pragma unroll
         for (int e = 0; e < 8; ++e) vt[(int64_t)e * BS] = (uint16_t)(vv[e >> 1] >> (16 * (e & 1)));
     } else {

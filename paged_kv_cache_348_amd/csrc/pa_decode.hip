@@ -73,6 +73,10 @@ struct DecodeCfg {
     static constexpr int NE = STEP / BS > 0 ? STEP / BS : 1;  // table entries a step touches
     static constexpr int64_t TILE = (int64_t)D * BS;    // elements of one (block, head) tile
     typedef u32x4 QRegs[NKC];                           // query operand of one lane
+    // bf16 with blocks of 16 or 32 tokens: values are stored with bits 2 and 3
+    // of the in-block offset swapped, so a lane's 8 value tokens are one
+    // 16-byte load (see the layout notes in include/pa.h)
+    static constexpr bool VIL = BF16 && BS >= 16;
     static_assert(D % 32 == 0 && BS % 8 == 0, "shape");
 };
 
@@ -139,9 +143,11 @@ __device__ __forceinline__ void issue_step_e(StepRegs<BF16, D, BS>& r, const cha
     const int last = L - 1;
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
-        // key row n of tile t is token tok0 + 16 t + n: for a fixed lane group
-        // the 16 rows are 256 contiguous bytes of one chunk column
-        const int tok = min(tok0 + 16 * t + n, last);  // rows past the end read a valid slot, masked later
+        // key row n of tile t: with the interleaved value layout, step token
+        // 16 (n / 8) + 8 t + n % 8, else 16 t + n.  Either way the rows a lane
+        // group reads in one instruction are whole 128-byte lines of a chunk column.
+        const int srow = C::VIL ? 16 * (n >> 3) + 8 * t + (n & 7) : 16 * t + n;
+        const int tok = min(tok0 + srow, last);  // rows past the end read a valid slot, masked later
         const int32_t phys = pick_block<C::NE, BS>(e, tok, tok0);
         const char* kp = kbase + (int64_t)phys * blk_bytes + (int64_t)(tok % BS) * 16;
 #pragma unroll
@@ -150,7 +156,21 @@ __device__ __forceinline__ void issue_step_e(StepRegs<BF16, D, BS>& r, const cha
             r.k[t][c] = ld16_stream(kp + (int64_t)chunk * BS * 16);
         }
     }
-    if constexpr (BF16) {
+    if constexpr (C::VIL) {
+        // values: lane group j holds the scores of step tokens
+        // 16 (j / 2) + 4 (j % 2) + {0..3} and the same + 8, which the
+        // interleaved layout stores as the 8 slots from (tok0 + 8 j) % BS of
+        // head-dim row d: one 16-byte load.  A group whose first token is past
+        // the end has no valid token: it reads a group of the last token's
+        // block instead (masked later).
+        const int tv = (tok0 + 16 * (j >> 1) <= last) ? tok0 + 8 * j : (last & ~7);
+        const char* vp = vbase + (int64_t)pick_block<C::NE, BS>(e, tv, tok0) * blk_bytes + (int64_t)(tv % BS) * 2;
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) {
+            const int64_t d = 16 * c + n;
+            r.v[c] = ld16_stream(vp + d * BS * 2);
+        }
+    } else if constexpr (BF16) {
         // values: lane group j reads tokens tok0 + 4j .. +3 (tile 0) and
         // tok0 + 16 + 4j .. +3 (tile 1) of head-dim row d, the tokens whose
         // scores it holds; one 8-byte load each
@@ -217,7 +237,8 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
     using C = DecodeCfg<BF16, D, BS>;
     const bool tail = tok0 + C::STEP > L;
     if constexpr (BF16) {
-        // ---- scores: two 16-token tiles; lane (n, j) receives tokens 4j+i (tile a) and 16+4j+i (tile b)
+        // ---- scores: two 16-token tiles (rows as in issue_step_e); lane (n, j)
+        // receives rows 4j+i of tile a and of tile b
         f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < C::NKC; ++c) {
@@ -235,8 +256,12 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
         }
         if (tail) {
             // element e of the lane's scores / value operand is token tok(e)
-            const int base = tok0 + 4 * j;
-            auto tok = [&](int e) { return base + (e & 3) + ((e >> 2) << 4); };
+            // element e (score and value operand) of lane group j is step token
+            // tok(e); tile 1 holds the second four
+            auto tok = [&](int e) {
+                return C::VIL ? tok0 + 16 * (j >> 1) + 4 * (j & 1) + (e & 3) + 8 * (e >> 2)
+                              : tok0 + 4 * j + (e & 3) + 16 * (e >> 2);
+            };
             uint32_t keep[4];
 #pragma unroll
             for (int e = 0; e < 8; ++e) s[e] = (tok(e) < L) ? s[e] : -INFINITY;

@@ -261,3 +261,18 @@ def test_stream_read_validation():
     assert _l().pa_bench_stream_read(fake(), 17, fake(), 0, None) == pa.PA_ERR_INVALID_ARG
     assert _l().pa_bench_stream_read(fake(), 16, fake(), -1, None) == pa.PA_ERR_INVALID_ARG
     assert _l().pa_bench_stream_read(fake(), 0, fake(), 0, None) == pa.PA_OK
+
+
+def test_value_position_permutes_each_block():
+    import torch
+    for bs in (8, 16, 32):
+        for dt in (torch.bfloat16, torch.float32):
+            pos = [pa.value_position(o, bs, dt) for o in range(bs)]
+            assert sorted(pos) == list(range(bs))
+            assert all(pa.value_position(p, bs, dt) == o for o, p in enumerate(pos))  # an involution
+            if dt == torch.float32 or bs == 8:
+                assert pos == list(range(bs))
+            else:
+                # within each 16 offsets: 0-3, 8-11, 4-7, 12-15
+                assert pos[:16] == [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
+                assert all(p // 16 == o // 16 for o, p in enumerate(pos))

@@ -70,7 +70,7 @@ def test_full_size_sampled_rows(name, ps, nsample):
         # the decode token of sequence b sits in its slot, bit for bit
         blk, off = divmod(int(dev.host_dec_slots[b]), w.block_size)
         key = dev.k_cache[blk, :, :, off, :].reshape(w.num_kv_heads, w.head_dim)
-        val = dev.v_cache[blk, :, :, off]
+        val = dev.v_cache[blk, :, :, pa.value_position(off, w.block_size, dev.v_cache.dtype)]
         assert np.array_equal(bits(key), K[-1]), "decode-token key not in its slot"
         assert np.array_equal(bits(val), V[-1]), "decode-token value not in its slot"
     w.drop_kv()
