@@ -30,7 +30,7 @@ BAL = pa.PA_PARTITION_BALANCED
 CASES = [
     ("llama3_8b", BAL, 6),
     ("llama_70b", BAL, 4),
-    ("prefix_share", BAL, 6),
+    ("prefix_share", 512, 6),
     ("long_ctx_bs8", 512, 2),
     ("long_ctx_bs16", 512, 2),
     ("long_ctx_bs32", 512, 2),
