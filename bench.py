@@ -79,7 +79,7 @@ def measured_traffic(workload: str):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip().split()[0] if v.strip() else ""
     h = hashlib.sha256()
-    for f in ("pa_decode.hip", "pa_device.h"):
+    for f in ("pa_decode.hip", "pa_decode_common.h", "pa_device.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_348_amd", "csrc", f), "rb").read())
     if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
         return None
