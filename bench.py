@@ -43,6 +43,9 @@ PARTITION_BALANCED = -1  # the library's balanced split (PA_PARTITION_BALANCED)
 # samples of one prompt together, so their shared blocks are read while
 # still in L2 / MALL)
 DEFAULT_PARTITION = {"llama3_8b": PARTITION_BALANCED, "llama_70b": PARTITION_BALANCED, "prefix_share": 512}
+# decode entry point per workload: with prefix sharing, the shared-prefix
+# decode reads each prompt's blocks once for all of its samples
+DEFAULT_DECODE = {"prefix_share": "shared"}
 WORKLOAD_TEXT = {
     "llama3_8b": "Llama-3-8B-shaped decode layer: batch 64, 32 q / 8 kv heads (GQA 4), d_head 128, block 16, "
                  "bf16, seq_lens U[512,4096], seeded random block permutation of a pool = demand + 10%",
@@ -63,14 +66,15 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, mode: str = "split"):
     """HBM bytes per decode launch from the committed counter summary of this
     workload (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by their
     calibrations), or None when there is none or the decode sources changed
     since it was taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_counters.txt")
+    kernel = "pa_decode_shared_prefix" if mode == "shared" else "pa_decode"
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -79,7 +83,8 @@ def measured_traffic(workload: str):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip().split()[0] if v.strip() else ""
     h = hashlib.sha256()
-    for f in ("pa_decode.hip", "pa_decode_common.h", "pa_device.h"):
+    srcs = ("pa_shared.hip" if mode == "shared" else "pa_decode.hip", "pa_decode_common.h", "pa_device.h")
+    for f in srcs:
         h.update(open(os.path.join(ROOT, "paged_kv_cache_348_amd", "csrc", f), "rb").read())
     if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
         return None
@@ -158,7 +163,18 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_passes: int = 10000):
 # ---------------------------------------------------------------------------- GPU
 
 
-def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int = 20):
+def shared_read_bytes(w, plan) -> int:
+    """KV bytes the shared-prefix decode must read: each group's shared part
+    once, plus every request's own tokens."""
+    a = max(32, w.block_size)
+    per_tok = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    shared = (plan.prefix_blocks.astype(np.int64) * w.block_size) // a * a
+    own = int((w.seq_lens.astype(np.int64) - shared).sum())
+    once = sum(int(shared[s0]) for s0, _ in plan.groups)
+    return (own + once) * per_tok
+
+
+def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str, cold_iters: int = 20):
     import torch
 
     from paged_kv_cache_348_amd.workload import build_device_batch
@@ -171,9 +187,21 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
     log(f"device pool built in {time.perf_counter() - t0:.1f}s, NB {w.num_blocks}, width {dev.max_blocks}")
     w.drop_kv()
     stream = torch.cuda.current_stream()
+    plan = None
+    if decode_mode == "shared":
+        plan = dev.shared_plan()
+        log(f"shared-prefix plan: {plan.num_groups} groups, up to {plan.max_group} requests, "
+            f"up to {plan.max_prefix_blocks} shared blocks")
+        attend = lambda: dev.attend_shared(plan, partition_size=partition_size)  # noqa: E731
+    else:
+        attend = dev.attend
+
+    def step():
+        dev.cache_append()
+        attend()
 
     for _ in range(warmup):
-        dev.step()
+        step()
     torch.cuda.synchronize()
 
     # timed region: `steps` whole steps (cache append + decode)
@@ -182,7 +210,7 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
     t_wall = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
-        dev.step()
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -198,7 +226,7 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
         torch.cuda.synchronize()
         a.record(stream)
         for _ in range(n):
-            dev.attend()
+            attend()
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
@@ -209,7 +237,7 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
         for a, b in evs:
             scratch.amax()
             a.record(stream)
-            dev.attend()
+            attend()
             b.record(stream)
         torch.cuda.synchronize()
         t = np.array([a.elapsed_time(b) for a, b in evs])
@@ -222,7 +250,8 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
     # calibration: a plain streaming read of the same byte count
     import paged_kv_cache_348_amd as pa
 
-    nbytes = (w.kv_read_bytes() + 4095) // 4096 * 4096
+    read_bytes = shared_read_bytes(w, plan) if plan is not None else w.kv_read_bytes()
+    nbytes = (read_bytes + 4095) // 4096 * 4096
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     for _ in range(3):
@@ -248,7 +277,8 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, cold_iters: int =
     ms_append = ca0.elapsed_time(ca1) / steps
     return dict(ms_step=ms_step, wall_s=t_wall, hot_ms=hot, cold_ms=cold, ms_append=ms_append, out=out,
                 stream_read_gbps=nbytes / (sr_ms * 1e-3) / 1e9,
-                device=dev_name, width=dev.max_blocks, launches=dev.launches)
+                device=dev_name, width=dev.max_blocks, launches=dev.launches,
+                read_bytes=read_bytes)
 
 
 def main(argv=None):
@@ -258,6 +288,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--decode", choices=("split", "shared"), default=None,
+                    help="split: pa_decode; shared: pa_decode_shared_prefix (reads blocks shared by forked "
+                         "requests once per group); default: shared for prefix_share, else split")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--block-order", choices=("seeded", "identity"), default="seeded",
@@ -278,22 +311,26 @@ def main(argv=None):
     if args.block_order == "identity":
         w.free_order = np.arange(w.num_blocks, dtype=np.int32)
     ps = args.partition_size
+    mode = args.decode or DEFAULT_DECODE.get(args.workload, "split")
     if ps is None:
         ps = w.partition_size or DEFAULT_PARTITION.get(args.workload, 0)
+    if mode == "shared" and ps <= 0:
+        ps = 512
     kv_bytes = w.kv_read_bytes()
     log(f"workload {w.name}: B {w.batch}, sum L {int(w.seq_lens.sum())}, KV bytes {kv_bytes / 1e9:.3f} GB, "
-        f"partition {ps}")
+        f"partition {ps}, decode {mode}")
 
     cpu, ref = (None, None)
     if not args.no_cpu:
         cpu, ref = cpu_baseline(w, min_seconds=args.cpu_seconds)
         log(f"cpu oracle: {cpu['value']:.1f} tok/s on {cpu['cores']} cores")
 
-    g = gpu_bench(w, args.steps, args.warmup, ps)
+    g = gpu_bench(w, args.steps, args.warmup, ps, mode)
     ms = g["ms_step"]
     hot, cold = g["hot_ms"], g["cold_ms"]
     t_dec = float(np.median(hot)) * 1e-3
-    achieved = kv_bytes / t_dec / 1e9
+    read_bytes = g["read_bytes"]  # what the decode must read: logical KV bytes, or unique ones when shared
+    achieved = read_bytes / t_dec / 1e9
     err = None
     if ref is not None:
         err = float(np.abs(g["out"] - ref).max())
@@ -324,10 +361,14 @@ def main(argv=None):
             "block_size": w.block_size,
             "num_blocks": w.num_blocks,
             "partition_size": ps,
-            "step": "pa_cache_write (decode tokens) + pa_decode",
+            "step": "pa_cache_write (decode tokens) + "
+                    + ("pa_decode_shared_prefix" if mode == "shared" else "pa_decode"),
+            "decode": mode,
             "block_order": args.block_order,
         },
         "kv_read_gbps_step": kv_bytes / (ms * 1e-3) / 1e9,
+        "kv_logical_bytes": kv_bytes,
+        "kv_unique_read_bytes": read_bytes,
         "kv_read_frac_of_8tbs_step": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "decode_us": {"hot": float(np.median(hot)) * 1e3, "hot_runs": [float(x) * 1e3 for x in hot],
                       "cold_median": float(np.median(cold)) * 1e3, "cold_min": float(cold.min()) * 1e3},
@@ -336,13 +377,15 @@ def main(argv=None):
         "kv_tokens_per_s": float(w.seq_lens.sum()) / t_dec,
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode",
+            "kernel": "pa_decode_shared_prefix" if mode == "shared" else "pa_decode",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(args.workload) if ps == DEFAULT_PARTITION.get(args.workload, ps) else None,
-            "algorithmic_bytes_per_launch": kv_bytes,
+            "traffic": (measured_traffic(args.workload, mode)
+                        if ps == DEFAULT_PARTITION.get(args.workload, ps)
+                        and mode == DEFAULT_DECODE.get(args.workload, "split") else None),
+            "algorithmic_bytes_per_launch": read_bytes,
             "flop_per_launch": flop,
         },
         "cpu_baseline": cpu,

@@ -167,6 +167,73 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
+ * Shared-prefix decode: the same result as pa_decode (same arguments, same
+ * output, same handling of empty rows and bad tables), computed so that
+ * the keys and values of blocks that several requests share are read once
+ * for all of them.  Requests forked from one prompt point their tables at
+ * the same physical blocks ("Paged attention in LLMs", "Sharing blocks";
+ * MCQ page, comparison table, parallel sampling and beam search), so their
+ * attention over those blocks can be computed together: one wave loads a
+ * key/value step once and scores it against every member's queries.
+ *
+ *   groups        device, int32 [num_groups][2] = (first request, member
+ *                 count).  Members are requests first .. first + count - 1;
+ *                 groups do not overlap; requests in no group are allowed.
+ *   prefix_blocks device, int32 [num_seqs]: for a group member, the number
+ *                 of leading table entries the whole group has in common
+ *                 (the same for every member, at most
+ *                 floor(L_b / block_size) for each of them); 0 for a request
+ *                 in no group.
+ *   max_group_size >= every member count; max_group_size * (num_q_heads /
+ *                 num_kv_heads) <= 64 (<= 32 for PA_F32 with head_dim 128).
+ *   max_prefix_blocks >= every prefix_blocks entry, <= max_blocks_per_seq.
+ *   partition_size  as for pa_decode's fixed partitions (a multiple of 32
+ *                 and of block_size, at most 64 * block_size); both the
+ *                 shared part and each request's own part are cut into
+ *                 partitions of this many tokens.
+ * The first (prefix_blocks * block_size) / a * a tokens of a member, with
+ * a = max(32, block_size), are the shared part; the rest of its tokens are
+ * its own.  A prefix_blocks entry above max_prefix_blocks, or a shared
+ * part longer than the request, gives NaN rows; a group larger than
+ * max_group_size gives NaN rows for its members.  A group that breaks the
+ * rules above (members with different prefix_blocks, overlapping groups,
+ * tables that differ inside the shared part) gives unspecified values in
+ * its members' rows but reads and writes nothing outside the buffers.
+ * workspace: device, 256-byte aligned, at least
+ * pa_decode_shared_prefix_workspace_bytes() bytes of scratch (contents on
+ * entry do not matter); calls sharing a workspace must not overlap.
+ * ------------------------------------------------------------------------ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t max_blocks_per_seq,
+                                               int32_t max_prefix_blocks, int32_t partition_size);
+
+pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  int32_t num_kv_heads, float scale, void* out, void* stream,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                  pa_dtype dtype, const int32_t* groups, const int32_t* prefix_blocks,
+                                  int32_t num_groups, int32_t max_group_size, int32_t max_prefix_blocks,
+                                  int32_t partition_size, void* workspace, size_t workspace_bytes);
+
+/* Host planning for pa_decode_shared_prefix (host memory throughout, no HIP
+ * calls).  Walks the batch in order and grows a group from each request
+ * while the next request's table starts with the same entries: a request
+ * joins when the group then still shares at least min_shared_blocks whole
+ * blocks (blocks inside every member's length) and the reads saved,
+ * (members - 1) * shared blocks, do not go down; at most max_group_size
+ * members.  Only groups of two or more are listed.
+ *   block_tables  host int32 [num_seqs][max_blocks_per_seq];  seq_lens host int32 [num_seqs]
+ *   groups        out, host int32 [2 * num_seqs] (room for the worst case)
+ *   prefix_blocks out, host int32 [num_seqs]
+ *   *num_groups, *max_group (>= 1), *max_prefix_blocks   out
+ * ------------------------------------------------------------------------ */
+pa_status pa_plan_shared_prefix(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                int32_t max_blocks_per_seq, int32_t block_size, int32_t max_group_size,
+                                int32_t min_shared_blocks, int32_t* groups, int32_t* prefix_blocks,
+                                int32_t* num_groups, int32_t* max_group, int32_t* max_prefix_blocks);
+
+/* ------------------------------------------------------------------------
  * Host block allocator (no device memory, no HIP calls; not thread-safe).
  * Follows "Paged attention in LLMs" ("The fix", "Keeping track: the block
  * table", "Sharing blocks") and the MCQ page's copy-on-write row:

@@ -28,7 +28,8 @@ __all__ = [
     "PAError", "Allocator", "cache_write", "copy_blocks", "decode", "decode_workspace_bytes", "new_kv_cache",
     "kv_cache_shapes", "logical_view", "value_position", "stream_read", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_OOM",
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
-    "new_workspace",
+    "new_workspace", "SharedPrefixPlan", "plan_shared_prefix", "decode_shared_prefix",
+    "decode_shared_prefix_workspace_bytes", "shared_prefix_max_group",
 ]
 
 
@@ -191,6 +192,108 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale
                           _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), hkv, float(scale),
                           _dev(out, "out"), _stream_ptr(stream), B, hq, d, bs, nb, mb, _dtype_code(q.dtype),
                           partition_size, ws_ptr, ws_bytes), "pa_decode")
+    return out
+
+
+class SharedPrefixPlan:
+    """Groups of consecutive requests whose block tables start alike (pa_plan_shared_prefix).
+
+    Host arrays: ``groups`` int32 [num_groups, 2] (first request, members),
+    ``prefix_blocks`` int32 [B]; ``to(device)`` adds their device copies.
+    """
+
+    def __init__(self, groups, prefix_blocks, max_group: int, max_prefix_blocks: int):
+        self.groups = groups
+        self.prefix_blocks = prefix_blocks
+        self.max_group = int(max_group)
+        self.max_prefix_blocks = int(max_prefix_blocks)
+        self.d_groups = None
+        self.d_prefix_blocks = None
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.groups.shape[0])
+
+    def to(self, device="cuda"):
+        torch = _torch()
+        g = self.groups if self.num_groups else np.zeros((1, 2), dtype=np.int32)
+        self.d_groups = torch.from_numpy(np.ascontiguousarray(g)).to(device)
+        self.d_prefix_blocks = torch.from_numpy(np.ascontiguousarray(self.prefix_blocks)).to(device)
+        return self
+
+
+def shared_prefix_max_group(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype) -> int:
+    """Largest group pa_decode_shared_prefix takes for this shape: 64 query
+    columns per wave (32 for float32 with head dim 128) over the group's heads."""
+    cols = 32 if (_dtype_code(dtype) == PA_F32 and head_dim == 128) else 64
+    return max(1, cols // (num_q_heads // num_kv_heads))
+
+
+def plan_shared_prefix(block_tables, seq_lens, block_size: int, max_group_size: int,
+                       min_shared_blocks: int = 1) -> SharedPrefixPlan:
+    """Plan the shared-prefix decode of a batch from its host tables (int32 [B, W]) and lengths."""
+    tables = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if tables.ndim != 2 or lens.shape != (tables.shape[0],):
+        raise ValueError("block_tables must be [B, W] and seq_lens [B]")
+    B, W = tables.shape
+    groups = np.zeros(2 * max(B, 1), dtype=np.int32)
+    pblk = np.zeros(max(B, 1), dtype=np.int32)
+    ng, mg, mp = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    check(lib().pa_plan_shared_prefix(tables.ctypes.data_as(P_I32), lens.ctypes.data_as(P_I32), B, W, block_size,
+                                      max_group_size, min_shared_blocks, groups.ctypes.data_as(P_I32),
+                                      pblk.ctypes.data_as(P_I32), ctypes.byref(ng), ctypes.byref(mg),
+                                      ctypes.byref(mp)), "pa_plan_shared_prefix")
+    return SharedPrefixPlan(groups[:2 * ng.value].reshape(ng.value, 2).copy(), pblk[:B].copy(), mg.value, mp.value)
+
+
+def decode_shared_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, block_size: int,
+                                         max_blocks_per_seq: int, max_prefix_blocks: int,
+                                         partition_size: int) -> int:
+    return int(lib().pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size,
+                                                             max_blocks_per_seq, max_prefix_blocks, partition_size))
+
+
+def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale: float,
+                         plan: SharedPrefixPlan, partition_size: int = 512, out=None, workspace=None, stream=None,
+                         max_group_size: Optional[int] = None):
+    """Decode attention that reads blocks shared by a plan's groups once per group (pa_decode_shared_prefix).
+
+    ``plan`` must hold device copies (``plan.to(device)``).  Returns ``out``.
+    ``max_group_size`` overrides the plan's (to size the launch for a larger bound).
+    """
+    torch = _torch()
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    if hkv != num_kv_heads:
+        raise ValueError("num_kv_heads does not match the cache")
+    B, hq, dq = q.shape
+    if dq != d or q.dtype != k_cache.dtype:
+        raise ValueError("q must be [B, Hq, head_dim] in the cache dtype")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("seq_lens must be int32 [B]")
+    if plan.d_groups is None or plan.d_prefix_blocks is None:
+        raise ValueError("plan has no device copies: call plan.to(device)")
+    if plan.d_prefix_blocks.numel() != B:
+        raise ValueError("plan was made for another batch")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    mb = block_tables.shape[1]
+    mg = plan.max_group if max_group_size is None else int(max_group_size)
+    need = decode_shared_prefix_workspace_bytes(B, hq, d, bs, mb, plan.max_prefix_blocks, partition_size) if B else 0
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = new_workspace(need, q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    check(lib().pa_decode_shared_prefix(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+        _dev(seq_lens, "seq_lens"), hkv, float(scale), _dev(out, "out"), _stream_ptr(stream), B, hq, d, bs, nb, mb,
+        _dtype_code(q.dtype), _dev(plan.d_groups, "groups"), _dev(plan.d_prefix_blocks, "prefix_blocks"),
+        plan.num_groups, mg, plan.max_prefix_blocks, partition_size, ws_ptr, ws_bytes), "pa_decode_shared_prefix")
     return out
 
 

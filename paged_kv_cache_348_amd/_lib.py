@@ -32,6 +32,14 @@ SIGNATURES = [
     ("pa_decode", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                             c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                             c_void_p, c_size_t]),
+    ("pa_decode_shared_prefix_workspace_bytes", c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                           c_int32]),
+    ("pa_decode_shared_prefix", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                                          c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                          c_int32, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                          c_size_t]),
+    ("pa_plan_shared_prefix", c_int32, [P_I32, P_I32, c_int32, c_int32, c_int32, c_int32, c_int32, P_I32, P_I32,
+                                        P_I32, P_I32, P_I32]),
     ("pa_alloc_create", c_void_p, [c_int32, c_int32, P_I32]),
     ("pa_alloc_destroy", None, [c_void_p]),
     ("pa_alloc_add_seq", c_int32, [c_void_p, c_int64]),

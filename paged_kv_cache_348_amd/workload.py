@@ -16,7 +16,8 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-from . import Allocator, cache_write, copy_blocks, decode, decode_workspace_bytes, new_kv_cache, new_workspace
+from . import (Allocator, cache_write, copy_blocks, decode, decode_shared_prefix, decode_shared_prefix_workspace_bytes,
+               decode_workspace_bytes, new_kv_cache, new_workspace, plan_shared_prefix, shared_prefix_max_group)
 
 
 def _torch():
@@ -53,6 +54,7 @@ class DeviceBatch:
     host_lens: np.ndarray
     host_dec_slots: np.ndarray
     launches: dict = field(default_factory=dict)
+    shared_workspace: Optional[object] = None
 
     @property
     def max_blocks(self) -> int:
@@ -73,6 +75,28 @@ class DeviceBatch:
                 self.workspace = ws
         return decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, w.num_kv_heads, w.scale,
                       out=self.out if out is None else out, partition_size=ps, workspace=ws, stream=stream)
+
+    def shared_plan(self, max_group_size: Optional[int] = None, min_shared_blocks: int = 1):
+        """Plan (host) and upload the shared-prefix grouping of this batch's tables."""
+        w = self.workload
+        mg = (shared_prefix_max_group(w.num_q_heads, w.num_kv_heads, w.head_dim, self.q.dtype)
+              if max_group_size is None else max_group_size)
+        plan = plan_shared_prefix(self.host_tables, self.host_lens, w.block_size, mg, min_shared_blocks)
+        return plan.to(self.q.device)
+
+    def attend_shared(self, plan, partition_size: int = 512, stream=None, out=None, workspace=None):
+        """Decode attention through the shared-prefix path (pa_decode_shared_prefix)."""
+        w = self.workload
+        ws = workspace
+        if ws is None:
+            need = decode_shared_prefix_workspace_bytes(w.batch, w.num_q_heads, w.head_dim, w.block_size,
+                                                        self.max_blocks, plan.max_prefix_blocks, partition_size)
+            ws = self.shared_workspace
+            if need and (ws is None or ws.numel() < need):
+                ws = self.shared_workspace = new_workspace(need, self.q.device)
+        return decode_shared_prefix(self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                                    w.num_kv_heads, w.scale, plan, partition_size=partition_size,
+                                    out=self.out if out is None else out, workspace=ws, stream=stream)
 
     def step(self, stream=None, partition_size: Optional[int] = None):
         """One decode step: append the decode tokens, then attend."""

@@ -293,7 +293,8 @@ def llama_70b(seed: int = 0, batch: int = 256, len_lo: int = 1024, len_hi: int =
 
 
 def prefix_share(seed: int = 0, prompts: int = 32, samples: int = 8, prompt_len: int = 2040,
-                 tail_max: int = 512, **_):
+                 tail_max: int = 512, block_size: int = 16, dtype: str = "bf16", num_q_heads: int = 32,
+                 num_kv_heads: int = 8, head_dim: int = 128, **_):
     """Parallel sampling: each prompt is stored once and forked to every sample.
 
     Sample s of prompt p is sequence ``samples*p + s``.  Sample 0 prefills the
@@ -301,8 +302,10 @@ def prefix_share(seed: int = 0, prompts: int = 32, samples: int = 8, prompt_len:
     count generated tokens before the measured step.  At step k = 1, 2, ...
     every sample with k <= t+1 appends one token, in sequence-id order; the
     token of step t+1 is that sample's decode token.  L = prompt_len + t + 1.
+    The shape keywords exist for small parity cases; the defaults are the
+    measured workload.
     """
-    cfg, bs = 3, 16
+    cfg, bs = 3, block_size
     B = prompts * samples
     tails = _rng(seed, cfg, S_TAILS).integers(0, tail_max + 1, size=B).astype(np.int64)
     ops: List[Op] = []
@@ -321,11 +324,12 @@ def prefix_share(seed: int = 0, prompts: int = 32, samples: int = 8, prompt_len:
     bound = prompts * (-(-prompt_len // bs)) + sum(-(-(int(L) - base) // bs) for L in lens)
     num_blocks = int(math.ceil(1.1 * bound))
     w = Workload(
-        name="prefix_share", config_id=cfg, seed=seed, dtype="bf16", num_q_heads=32, num_kv_heads=8,
-        head_dim=128, block_size=bs, num_blocks=num_blocks, scale=1.0 / math.sqrt(128),
+        name="prefix_share", config_id=cfg, seed=seed, dtype=dtype, num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=bs, num_blocks=num_blocks,
+        scale=1.0 / math.sqrt(head_dim),
         partition_size=0, seq_ids=list(range(B)), seq_lens=lens,
         free_order=_rng(seed, cfg, S_FREE_ORDER).permutation(num_blocks).astype(np.int32),
-        ops=ops, q=_draw_q(seed, cfg, B, 32, 128, "bf16"),
+        ops=ops, q=_draw_q(seed, cfg, B, num_q_heads, head_dim, dtype),
     )
 
     def runs(seq, a, e):

@@ -276,3 +276,134 @@ def test_value_position_permutes_each_block():
                 # within each 16 offsets: 0-3, 8-11, 4-7, 12-15
                 assert pos[:16] == [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
                 assert all(p // 16 == o // 16 for o, p in enumerate(pos))
+
+
+# ---------------------------------------------------------------- shared-prefix decode (host side)
+def shared_call(**kw):
+    a = dict(q=fake(), kc=fake(), vc=fake(), bt=fake(), sl=fake(), hkv=8, scale=0.1, out=fake(), stream=None,
+             B=16, hq=32, d=128, bs=16, nb=100, mb=40, dt=1, groups=fake(), pblk=fake(), ng=2, mg=8, mp=30, ps=512,
+             ws=fake(0x10000), wsb=1 << 30)
+    a.update(kw)
+    return _l().pa_decode_shared_prefix(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["hkv"], a["scale"], a["out"],
+                                        a["stream"], a["B"], a["hq"], a["d"], a["bs"], a["nb"], a["mb"], a["dt"],
+                                        a["groups"], a["pblk"], a["ng"], a["mg"], a["mp"], a["ps"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(mg=17), pa.PA_ERR_UNSUPPORTED),                # 17 requests x 4 heads > 64 columns
+    (dict(mg=9, dt=0), pa.PA_ERR_UNSUPPORTED),           # float32, head dim 128: 32 columns at most
+    (dict(hq=8 * 17), pa.PA_ERR_UNSUPPORTED),
+    (dict(mg=0), pa.PA_ERR_INVALID_ARG),
+    (dict(mp=41), pa.PA_ERR_INVALID_ARG),                # prefix longer than the table
+    (dict(mp=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(ng=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(ng=17), pa.PA_ERR_UNSUPPORTED),                # more groups than requests
+    (dict(ps=0), pa.PA_ERR_UNSUPPORTED),
+    (dict(ps=48), pa.PA_ERR_UNSUPPORTED),
+    (dict(ps=-1), pa.PA_ERR_UNSUPPORTED),                # the balanced split is not offered here
+    (dict(groups=None), pa.PA_ERR_INVALID_ARG),
+    (dict(pblk=None), pa.PA_ERR_INVALID_ARG),
+    (dict(ws=None), pa.PA_ERR_INVALID_ARG),
+    (dict(wsb=64), pa.PA_ERR_INVALID_ARG),
+    (dict(ws=fake(0x10010)), pa.PA_ERR_INVALID_ARG),      # not 256-byte aligned
+    (dict(d=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(scale=float("inf")), pa.PA_ERR_INVALID_ARG),
+    (dict(B=0, q=None, kc=None, vc=None, bt=None, sl=None, out=None, groups=None, pblk=None, ng=0, ws=None),
+     pa.PA_OK),
+])
+def test_shared_prefix_decode_rejects_bad_arguments(kw, expect):
+    assert shared_call(**kw) == expect
+
+
+def test_shared_prefix_max_group():
+    import torch
+    assert pa.shared_prefix_max_group(32, 8, 128, torch.bfloat16) == 16
+    assert pa.shared_prefix_max_group(64, 8, 128, torch.bfloat16) == 8
+    assert pa.shared_prefix_max_group(64, 8, 128, torch.float32) == 4
+    assert pa.shared_prefix_max_group(8, 8, 64, torch.float32) == 64
+    assert pa.shared_prefix_max_group(16, 1, 64, torch.bfloat16) == 4
+
+
+def test_shared_prefix_workspace_size():
+    n = pa.decode_shared_prefix_workspace_bytes(16, 32, 128, 16, 40, 30, 512)
+    # prefix: 30 blocks of 16 = 480 tokens -> 1 partition; own part: 640 tokens -> 2 partitions
+    rows = 16 * 32 * 3
+    assert n >= rows * 128 * 4 + rows * 2 * 4 and n % 256 == 0
+    assert pa.decode_shared_prefix_workspace_bytes(16, 32, 128, 16, 40, 41, 512) == 0
+    assert pa.decode_shared_prefix_workspace_bytes(16, 32, 128, 16, 40, 30, 0) == 0
+
+
+def plan(tables, lens, bs=16, mg=8, mins=1):
+    p = pa.plan_shared_prefix(np.array(tables, dtype=np.int32), np.array(lens, dtype=np.int32), bs, mg, mins)
+    return [tuple(g) for g in p.groups.tolist()], p.prefix_blocks.tolist(), p.max_group, p.max_prefix_blocks
+
+
+def test_plan_groups_requests_with_common_leading_blocks():
+    # three requests share blocks 5, 6, 7; the fourth shares nothing
+    t = [[5, 6, 7, 10], [5, 6, 7, 11], [5, 6, 7, 12], [9, 1, 2, 3]]
+    assert plan(t, [64, 60, 50, 64]) == ([(0, 3)], [3, 3, 3, 0], 3, 3)
+    # the shared count stops at the blocks wholly inside the shortest member
+    assert plan(t, [64, 60, 40, 64]) == ([(0, 3)], [2, 2, 2, 0], 3, 2)
+    # a member whose length covers no whole block breaks the group (nothing shared)
+    assert plan(t, [64, 60, 15, 64]) == ([(0, 2)], [3, 3, 0, 0], 2, 3)
+    # min_shared_blocks
+    assert plan(t, [64, 64, 64, 64], mins=4) == ([], [0, 0, 0, 0], 1, 0)
+    # max_group_size caps a run of identical tables
+    same = [[1, 2, 3]] * 5
+    assert plan(same, [48] * 5, mg=2) == ([(0, 2), (2, 2)], [3, 3, 3, 3, 0], 2, 3)
+    # empty batch and one request
+    assert plan(np.zeros((0, 3)), [], mg=2) == ([], [], 1, 0)
+    assert plan([[1, 2]], [32]) == ([], [0], 1, 0)
+
+
+def test_plan_stops_when_a_join_would_save_fewer_reads():
+    # A and B share 10 blocks; C shares 2 with them: (2 members, 10 blocks) saves 10 reads,
+    # (3 members, 2 blocks) would save 4, so C starts its own group with D
+    A = list(range(100, 112))
+    B = A[:10] + [200, 201]
+    C = A[:2] + [300 + i for i in range(10)]
+    D = C[:8] + [400, 401, 402, 403]
+    g, p, mg, mp = plan([A, B, C, D], [192] * 4)
+    assert g == [(0, 2), (2, 2)] and p == [10, 10, 8, 8] and mg == 2 and mp == 10
+    # but a third member that keeps most of the shared blocks does join: 3 x 9 >= 2 x 10
+    E = A[:9] + [500, 501, 502]
+    g, p, _, _ = plan([A, B, E], [192] * 3)
+    assert g == [(0, 3)] and p == [9, 9, 9]
+
+
+def test_plan_on_the_prefix_sharing_workload():
+    w = make_workload("prefix_share", seed=0, prompts=4, samples=8, prompt_len=2040, tail_max=40)
+    a = pa.Allocator(w.num_blocks, w.block_size, w.free_order)
+    for op in w.ops:
+        if op.kind == "add":
+            a.add_seq(op.seq)
+        elif op.kind == "fork":
+            a.fork(op.parent, op.seq)
+        elif op.kind == "append":
+            a.append(op.seq, op.n)
+    tables, lens = a.batch_tables(w.seq_ids)
+    g, p, mg, mp = plan(tables, lens, mg=8)
+    # every sample of a prompt shares the prompt's 127 full blocks; the partial
+    # 128th was copied on write by all but the last sample
+    assert g == [(8 * i, 8) for i in range(4)] and p == [127] * 32 and mg == 8 and mp == 127
+
+
+def test_plan_rejects_bad_arguments():
+    t = np.zeros((2, 3), np.int32)
+    ln = np.zeros(2, np.int32)
+    g = np.zeros(4, np.int32)
+    pb = np.zeros(2, np.int32)
+    n1, n2, n3 = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    P = _lib.P_I32
+
+    def call(B=2, W=3, bs=16, mg=4, mins=1, groups=g):
+        return _l().pa_plan_shared_prefix(t.ctypes.data_as(P), ln.ctypes.data_as(P), B, W, bs, mg, mins,
+                                          groups.ctypes.data_as(P) if groups is not None else None,
+                                          pb.ctypes.data_as(P), ctypes.byref(n1), ctypes.byref(n2),
+                                          ctypes.byref(n3))
+    assert call() == pa.PA_OK
+    assert call(B=-1) == pa.PA_ERR_INVALID_ARG
+    assert call(bs=0) == pa.PA_ERR_INVALID_ARG
+    assert call(mg=0) == pa.PA_ERR_INVALID_ARG
+    assert call(mins=0) == pa.PA_ERR_INVALID_ARG
+    assert call(groups=None) == pa.PA_ERR_INVALID_ARG
