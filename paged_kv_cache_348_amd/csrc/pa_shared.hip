@@ -164,8 +164,8 @@ __global__ __launch_bounds__(64) void decode_suffix_kernel(
     int num_blocks, int PS, int P_pre, int P_max, float scale_log2) {
     using C = DecodeCfg<BF16, D, BS>;
     const int g = blockIdx.x;
-    const int p = blockIdx.y;
-    const int b = blockIdx.z;
+    const int b = blockIdx.y;
+    const int p = blockIdx.z;  // slowest: every request's first partition is dispatched first
     const int lane = threadIdx.x;
     const int n = lane & 15;
     const int j = lane >> 4;
@@ -189,74 +189,86 @@ __global__ __launch_bounds__(64) void decode_suffix_kernel(
     if (n < G) store_partial<BF16, D, BS>(part_o, part_ml, row0 + n, P_max, P_pre + p, S, j);
 }
 
-// One 256-lane workgroup per (query head, request): merges the request's
-// prefix partials [0, npre) and suffix partials [P_pre, P_pre + nsuf).
+// One wave per output row (request b, query head h), four rows per
+// workgroup: merges the request's prefix partials [0, npre) and its own
+// partials [P_pre, P_pre + nsuf).  Lane i holds partial i's (m, l) of the
+// current 64-partial window; each lane accumulates D / 64 dims, four
+// partials' loads in flight at a time.
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(256) void merge_shared_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            const int32_t* __restrict__ lens,
                                                            const int32_t* __restrict__ prefix_blocks,
-                                                           void* __restrict__ out_, int Hq, int max_blocks,
+                                                           void* __restrict__ out_, int B, int Hq, int max_blocks,
                                                            int max_pre, int PS, int P_pre, int P_max) {
-    const int h = blockIdx.x;
-    const int b = blockIdx.y;
-    const int64_t row = (int64_t)b * Hq + h;
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)B * Hq) return;
+    const int b = (int)(row / Hq);
     const int L = lens[b];
     const int pb = prefix_blocks[b];
     const bool ok = L > 0 && (int64_t)L <= (int64_t)max_blocks * BS && pb >= 0 && pb <= max_pre &&
                     shared_tokens<BS>(pb) <= L;
+    float res[PER];
     if (!ok) {
         // empty request: zero row; a length or prefix the table cannot hold: NaN row
-        if (threadIdx.x < D) {
-            const float v = L <= 0 ? 0.0f : __builtin_nanf("");
-            if constexpr (BF16)
-                reinterpret_cast<uint16_t*>(out_)[row * D + threadIdx.x] = (uint16_t)bf16_bits_rne(v);
-            else
-                reinterpret_cast<float*>(out_)[row * D + threadIdx.x] = v;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) res[e] = L <= 0 ? 0.0f : __builtin_nanf("");
+    } else {
+        const int T = shared_tokens<BS>(pb);
+        const int npre = (T + PS - 1) / PS;
+        const int np = npre + (L - T + PS - 1) / PS;
+        const float* ml = part_ml + row * P_max * 2;
+        const float* po = part_o + row * P_max * D + lane * PER;
+        auto slot = [&](int i) { return i < npre ? i : P_pre + (i - npre); };
+        float M = -INFINITY;
+        for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[2 * slot(i)]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
+        float num[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) num[e] = 0.f;
+        float den = 0.f;
+        for (int w0 = 0; w0 < np; w0 += 64) {
+            const int nw = min(64, np - w0);
+            float wl = 0.f;
+            if (lane < nw) {
+                const int si = slot(w0 + lane);
+                wl = ml[2 * si + 1] * __builtin_amdgcn_exp2f(ml[2 * si] - M);
+            }
+            den += wl;
+            for (int i0 = 0; i0 < nw; i0 += 4) {
+                float v[4][PER];
+                float wt[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = min(i0 + u, nw - 1);  // past the end: a valid slot, weight 0
+                    const float* src = po + (int64_t)slot(w0 + i) * D;
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) v[u][e] = src[e];
+                    const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+                    wt[u] = (i0 + u < nw) ? wi : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) num[e] += wt[u] * v[u][e];
+            }
         }
-        return;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) den += shfl_xor_f(den, o);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) res[e] = num[e] / den;
     }
-    const int T = shared_tokens<BS>(pb);
-    const int npre = (T + PS - 1) / PS;
-    const int nsuf = (L - T + PS - 1) / PS;
-    const int np = npre + nsuf;
-    auto slot = [&](int i) { return i < npre ? i : P_pre + (i - npre); };
-    const float* ml = part_ml + row * P_max * 2;
-    const float* po = part_o + row * P_max * D;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-
-    float M = -INFINITY;
-    for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[2 * slot(i)]);
+    if constexpr (BF16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(out_) + row * D + lane * PER;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-
-    constexpr int PER = D / 64;
-    float num[PER];
+        for (int e = 0; e < PER; ++e) o[e] = (uint16_t)bf16_bits_rne(res[e]);
+    } else {
+        float* o = reinterpret_cast<float*>(out_) + row * D + lane * PER;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] = 0.f;
-    float den = 0.f;
-    for (int i = w; i < np; i += 4) {
-        const int si = slot(i);
-        const float wt = ml[2 * si + 1] * __builtin_amdgcn_exp2f(ml[2 * si] - M);
-        den += wt;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) num[e] += wt * po[(int64_t)si * D + lane * PER + e];
-    }
-    __shared__ float s_num[4][D];
-    __shared__ float s_den[4];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) s_num[w][lane * PER + e] = num[e];
-    if (lane == 0) s_den[w] = den;
-    __syncthreads();
-    if (threadIdx.x < D) {
-        const int d = threadIdx.x;
-        const float total = s_den[0] + s_den[1] + s_den[2] + s_den[3];
-        const float v = (s_num[0][d] + s_num[1][d] + s_num[2][d] + s_num[3][d]) / total;
-        if constexpr (BF16)
-            reinterpret_cast<uint16_t*>(out_)[row * D + d] = (uint16_t)bf16_bits_rne(v);
-        else
-            reinterpret_cast<float*>(out_)[row * D + d] = v;
+        for (int e = 0; e < PER; ++e) o[e] = res[e];
     }
 }
 
@@ -322,13 +334,14 @@ hipError_t launch_shared(const SharedLaunch& a) {
         e = launch_prefix<BF16, D, BS, max_columns(BF16, D) / 16>(a);
     if (e != hipSuccess) return e;
     const int P_suf = a.P_max - a.P_pre;
-    hipLaunchKernelGGL((pa::decode_suffix_kernel<BF16, D, BS>), dim3((unsigned)a.Hkv, (unsigned)P_suf, (unsigned)a.B),
+    hipLaunchKernelGGL((pa::decode_suffix_kernel<BF16, D, BS>), dim3((unsigned)a.Hkv, (unsigned)a.B, (unsigned)P_suf),
                        dim3(64), 0, a.s, a.q, a.kc, a.vc, a.tables, a.lens, a.pblk, a.po, a.pml, a.Hq, a.Hkv,
                        a.Hq / a.Hkv, a.max_blocks, a.max_pre, a.num_blocks, a.PS, a.P_pre, a.P_max, a.sl2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((pa::merge_shared_kernel<BF16, D, BS>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(256), 0, a.s,
-                       a.po, a.pml, a.lens, a.pblk, a.out, a.Hq, a.max_blocks, a.max_pre, a.PS, a.P_pre, a.P_max);
+    const int64_t rows = (int64_t)a.B * a.Hq;
+    hipLaunchKernelGGL((pa::merge_shared_kernel<BF16, D, BS>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, a.s,
+                       a.po, a.pml, a.lens, a.pblk, a.out, a.B, a.Hq, a.max_blocks, a.max_pre, a.PS, a.P_pre, a.P_max);
     return hipGetLastError();
 }
 

@@ -74,3 +74,29 @@ def test_full_size_sampled_rows(name, ps, nsample):
         assert np.array_equal(bits(key), K[-1]), "decode-token key not in its slot"
         assert np.array_equal(bits(val), V[-1]), "decode-token value not in its slot"
     w.drop_kv()
+
+
+@pytest.mark.timeout(900)
+def test_full_size_shared_prefix_sampled_rows():
+    """The shared-prefix decode at the prefix-sharing workload's full size, as the benchmark launches it."""
+    w = make_workload("prefix_share", seed=0)
+    dev = build_device_batch(w, partition_size=512)
+    dev.cache_append()
+    plan = dev.shared_plan()
+    say("prefix_share shared: groups", plan.num_groups, "max group", plan.max_group, "prefix blocks",
+        plan.max_prefix_blocks)
+    assert plan.num_groups == 32 and plan.max_group == 8 and plan.max_prefix_blocks == 127
+    out = dev.attend_shared(plan, partition_size=512)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite output"
+    rng = np.random.default_rng(99)
+    rows = sorted({int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))}
+                  | set(int(x) for x in rng.choice(w.batch, size=8, replace=False)))
+    for b in rows:
+        K, V = w.sequence_kv(b)
+        ref = oa.dense_attention(oa.widen(w.q[b]), oa.widen(K), oa.widen(V), w.scale)
+        err = float(np.abs(got[b] - ref).max())
+        say("prefix_share shared row", b, "L", int(w.seq_lens[b]), "max abs err", f"{err:.3e}")
+        assert err <= TOL, (b, err)
+    w.drop_kv()

@@ -64,6 +64,7 @@ CASES = [
                           head_dim=64), (64,)),
     ("bf16-short-prompt", dict(prompts=2, samples=8, prompt_len=20, tail_max=30), (64,)),
     ("bf16-step-aligned", dict(prompts=2, samples=8, prompt_len=256, tail_max=0), (64, 512)),
+    ("bf16-many-partials", dict(prompts=1, samples=4, prompt_len=2500, tail_max=1200), (32,)),  # > 64 per row
     ("f32-G1-D64", dict(prompts=2, samples=5, prompt_len=150, tail_max=40, dtype="f32", num_q_heads=8,
                         head_dim=64), (32, 128)),
     ("f32-G4-D128", dict(prompts=2, samples=8, prompt_len=180, tail_max=30, dtype="f32"), (64,)),
