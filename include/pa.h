@@ -234,6 +234,55 @@ pa_status pa_plan_shared_prefix(const int32_t* block_tables, const int32_t* seq_
                                 int32_t* num_groups, int32_t* max_group, int32_t* max_prefix_blocks);
 
 /* ------------------------------------------------------------------------
+ * KV-memory accounting of a request trace (host only, no HIP calls): how
+ * much of the memory a scheme holds is filled with tokens, under the
+ * contiguous reservation the pages start from ("Paged attention in LLMs",
+ * "Why the memory gets wasted": each request reserves its prompt plus the
+ * largest reply in one unbroken run, placed first fit, so both unreached
+ * reserved slots and gaps too small for the next reservation are lost) and
+ * under paging ("The fix", "Why this helps so much": whole blocks taken one
+ * at a time from anywhere, at most the last block's unfilled tail lost per
+ * request; MCQ page, comparison table, "Memory waste" row).
+ *
+ * Time runs in decode steps.  At step t: requests that completed their
+ * reply at t - 1 release their memory; requests with arrival_step == t are
+ * admitted in trace order (the prompt is stored at once) or rejected if they
+ * do not fit (contiguous: no free run of prompt + max_reply slots, or a reply
+ * longer than max_reply; paged: fewer free blocks than the prompt needs);
+ * every request admitted before t appends one reply token (a paged request
+ * that needs a new block when none is free is dropped and releases its
+ * blocks); a request whose reply is complete releases at t + 1.  After each
+ * step the held and used slots of the live requests are summed.
+ *
+ *   arrival_step, prompt_len, reply_len  host int32 [num_requests], arrival
+ *                 steps non-decreasing (trace order) and >= 0, prompts >= 1,
+ *                 replies >= 0
+ *   capacity_slots  token slots of the memory (paged: capacity / block_size blocks)
+ *   scheme        PA_MEM_CONTIGUOUS (param = max_reply, the reserved reply
+ *                 length) or PA_MEM_PAGED (param = block_size >= 1)
+ *   out           host; filled on PA_OK
+ * ------------------------------------------------------------------------ */
+#define PA_MEM_CONTIGUOUS 0
+#define PA_MEM_PAGED 1
+
+typedef struct {
+    int64_t steps;              /* steps until the last request released (or the trace ended) */
+    int64_t used_slot_steps;    /* sum over steps of slots holding a token */
+    int64_t held_slot_steps;    /* sum over steps of slots held by live requests */
+    int64_t peak_used;          /* largest per-step used slots */
+    int64_t peak_held;          /* largest per-step held slots */
+    int64_t max_request_waste;  /* largest held - used of one request at the end of a step */
+    int32_t admitted;
+    int32_t rejected;           /* did not fit on arrival */
+    int32_t dropped;            /* paged: no block left while growing */
+    int32_t peak_live;          /* most requests holding memory at the end of a step */
+} pa_mem_stats;
+
+pa_status pa_simulate_memory(const int32_t* arrival_step, const int32_t* prompt_len, const int32_t* reply_len,
+                             int32_t num_requests, int64_t capacity_slots, int32_t scheme, int32_t param,
+                             pa_mem_stats* out);
+
+/* ------------------------------------------------------------------------
  * Host block allocator (no device memory, no HIP calls; not thread-safe).
  * Follows "Paged attention in LLMs" ("The fix", "Keeping track: the block
  * table", "Sharing blocks") and the MCQ page's copy-on-write row:

@@ -16,6 +16,9 @@ pages on PagedAttention describe, in float64 for floating point:
   each ``[num_blocks, num_kv_heads, block_size, head_dim]``), a NaN-poisoned
   pre-image, the slot scatter and whole-block copies, and a sequential replay
   of a workload's operation list.
+* ``memsim``: replay of a request trace (arrivals, prompts, replies) under
+  contiguous reservation and under paging, with the slot accounting of the
+  two allocator models (the pages' waste comparison).
 * ``attention``: the block-table walk that gathers K and V per position,
   followed by standard scaled-dot-product attention (dense two-pass softmax),
   a loop-only variant for tiny inputs, and the partition / log-sum-exp merge

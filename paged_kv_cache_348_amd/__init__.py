@@ -21,6 +21,7 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
+from ._lib import (PA_MEM_CONTIGUOUS, PA_MEM_PAGED, MemStats)
 from ._lib import (PA_BF16, PA_PARTITION_BALANCED, PA_ERR_EXISTS, PA_ERR_INVALID_ARG, PA_ERR_LAUNCH, PA_ERR_NOT_FOUND, PA_ERR_OOM,
                    PA_ERR_UNSUPPORTED, PA_F32, PA_OK, P_I32, P_I64, PAError, check, lib, status_string)
 
@@ -29,7 +30,8 @@ __all__ = [
     "kv_cache_shapes", "logical_view", "value_position", "stream_read", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_OOM",
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
     "new_workspace", "SharedPrefixPlan", "plan_shared_prefix", "decode_shared_prefix",
-    "decode_shared_prefix_workspace_bytes", "shared_prefix_max_group",
+    "decode_shared_prefix_workspace_bytes", "shared_prefix_max_group", "simulate_memory", "PA_MEM_CONTIGUOUS",
+    "PA_MEM_PAGED",
 ]
 
 
@@ -295,6 +297,21 @@ def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, num_kv_hea
         _dtype_code(q.dtype), _dev(plan.d_groups, "groups"), _dev(plan.d_prefix_blocks, "prefix_blocks"),
         plan.num_groups, mg, plan.max_prefix_blocks, partition_size, ws_ptr, ws_bytes), "pa_decode_shared_prefix")
     return out
+
+
+def simulate_memory(arrival, prompt, reply, capacity_slots: int, scheme: int, param: int) -> dict:
+    """KV-memory accounting of a request trace (pa_simulate_memory): ``scheme``
+    PA_MEM_CONTIGUOUS with ``param`` = reserved reply length, or PA_MEM_PAGED
+    with ``param`` = block size.  Returns the pa_mem_stats fields."""
+    arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.int32)) for x in (arrival, prompt, reply)]
+    n = arrs[0].shape[0]
+    if any(a.shape != (n,) for a in arrs):
+        raise ValueError("arrival, prompt and reply must be 1-D of one length")
+    st = MemStats()
+    check(lib().pa_simulate_memory(arrs[0].ctypes.data_as(P_I32), arrs[1].ctypes.data_as(P_I32),
+                                   arrs[2].ctypes.data_as(P_I32), n, int(capacity_slots), scheme, param,
+                                   ctypes.byref(st)), "pa_simulate_memory")
+    return {name: int(getattr(st, name)) for name, _ in MemStats._fields_}
 
 
 def stream_read(buf, sink, workgroups: int = 0, stream=None) -> None:

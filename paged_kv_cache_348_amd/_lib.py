@@ -19,6 +19,14 @@ P_I64 = ctypes.POINTER(ctypes.c_int64)
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_NOT_FOUND, PA_ERR_LAUNCH, PA_ERR_EXISTS = range(7)
 PA_F32, PA_BF16 = 0, 1
 PA_PARTITION_BALANCED = -1
+PA_MEM_CONTIGUOUS, PA_MEM_PAGED = 0, 1
+
+
+class MemStats(ctypes.Structure):
+    """pa_mem_stats (include/pa.h)."""
+    _fields_ = [("steps", c_int64), ("used_slot_steps", c_int64), ("held_slot_steps", c_int64),
+                ("peak_used", c_int64), ("peak_held", c_int64), ("max_request_waste", c_int64),
+                ("admitted", c_int32), ("rejected", c_int32), ("dropped", c_int32), ("peak_live", c_int32)]
 
 # (name, restype, argtypes) of every symbol include/pa.h and include/pa_bench.h declare
 SIGNATURES = [
@@ -40,6 +48,7 @@ SIGNATURES = [
                                           c_size_t]),
     ("pa_plan_shared_prefix", c_int32, [P_I32, P_I32, c_int32, c_int32, c_int32, c_int32, c_int32, P_I32, P_I32,
                                         P_I32, P_I32, P_I32]),
+    ("pa_simulate_memory", c_int32, [P_I32, P_I32, P_I32, c_int32, c_int64, c_int32, c_int32, c_void_p]),
     ("pa_alloc_create", c_void_p, [c_int32, c_int32, P_I32]),
     ("pa_alloc_destroy", None, [c_void_p]),
     ("pa_alloc_add_seq", c_int32, [c_void_p, c_int64]),

@@ -11,4 +11,6 @@ from .workloads import (  # noqa: F401
     make_workload,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
+    MemoryTrace,
+    memory_trace,
 )

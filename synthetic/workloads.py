@@ -49,6 +49,7 @@ S_Q = 3
 S_KV = 4
 S_TAILS = 5
 S_FINISH_ORDER = 6
+S_MEMTRACE = 7
 
 PROMPT_OWNER_BASE = 1 << 20  # KV owner id of prompt p in prefix sharing
 
@@ -374,3 +375,29 @@ def custom(seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim:
     nb = num_blocks if num_blocks is not None else _pool_for(lens, block_size, slack=1.25) + 2
     return _simple_batch("custom", config_id, seed, dtype, num_q_heads, num_kv_heads, head_dim,
                          block_size, lens, nb, partition_size)
+
+
+@dataclass
+class MemoryTrace:
+    """A request trace for the KV-memory accounting: arrival step, prompt and
+    reply lengths of each request, in arrival order."""
+    arrival: np.ndarray  # int32 [R], non-decreasing
+    prompt: np.ndarray  # int32 [R], >= 1
+    reply: np.ndarray  # int32 [R], 0 .. max_reply
+    max_reply: int
+
+
+def memory_trace(seed: int = 0, requests: int = 2000, mean_gap: float = 0.5, prompt_lo: int = 16,
+                 prompt_hi: int = 512, reply_mean: float = 300.0, max_reply: int = 2048) -> MemoryTrace:
+    """Seeded request trace.  The pages give no length distribution; this one
+    takes Poisson arrivals (exponential gaps of ``mean_gap`` steps, rounded
+    down), prompts uniform in [prompt_lo, prompt_hi] and replies exponential
+    with mean ``reply_mean`` rounded down and capped at ``max_reply`` (the
+    pages' example reserves 2,048 tokens for a reply)."""
+    g = _rng(seed, 100, S_MEMTRACE)
+    gaps = g.exponential(mean_gap, size=requests)
+    arrival = np.floor(np.cumsum(gaps)).astype(np.int64)
+    arrival -= arrival[0] if requests else 0
+    prompt = g.integers(prompt_lo, prompt_hi + 1, size=requests)
+    reply = np.minimum(np.floor(g.exponential(reply_mean, size=requests)), max_reply)
+    return MemoryTrace(arrival.astype(np.int32), prompt.astype(np.int32), reply.astype(np.int32), max_reply)
