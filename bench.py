@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 from synthetic import make_workload  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+HOST_LINK_GBPS = 64.0  # PCIe 5.0 x16, one direction
 PARTITION_BALANCED = -1  # the library's balanced split (PA_PARTITION_BALANCED)
 # launch configuration per workload, the faster mode as measured on MI355X
 # (the long-context ones use their own 512-token partitions with the
@@ -267,6 +268,33 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str,
     sr_ms = float(np.mean([a.elapsed_time(b) for a, b in sr]))
     del buf
 
+    # swap: the blocks of the first sequences out to a pinned host pool and
+    # back into the same blocks (the pool is unchanged afterwards)
+    nseq = min(8, w.batch)
+    blocks = sorted({int(b) for r in range(nseq) for b in dev.host_tables[r][: -(-int(dev.host_lens[r]) // w.block_size)]})
+    nsw = len(blocks)
+    ks, vs = pa.kv_cache_shapes(nsw, w.num_kv_heads, w.block_size, w.head_dim, dev.k_cache.dtype)
+    hk = torch.empty(ks, dtype=dev.k_cache.dtype, pin_memory=True)
+    hv = torch.empty(vs, dtype=dev.v_cache.dtype, pin_memory=True)
+    ids = torch.tensor(blocks, dtype=torch.int32)
+    seq = torch.arange(nsw, dtype=torch.int32)
+    out_pairs = torch.stack([ids, seq], 1).contiguous().cuda()
+    in_pairs = torch.stack([seq, ids], 1).contiguous().cuda()
+    swap = {}
+    for name, args in (("out", (dev.k_cache, dev.v_cache, hk, hv, out_pairs)),
+                       ("in", (hk, hv, dev.k_cache, dev.v_cache, in_pairs))):
+        pa.swap_blocks(*args)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            pa.swap_blocks(*args)
+        b.record(stream)
+        torch.cuda.synchronize()
+        swap[name] = a.elapsed_time(b) / 5
+    swap_bytes = nsw * 2 * w.num_kv_heads * w.block_size * w.head_dim * w.elem_bytes
+    del hk, hv
+
     # cache append alone
     ca0, ca1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ca0.record(stream)
@@ -278,7 +306,7 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str,
     return dict(ms_step=ms_step, wall_s=t_wall, hot_ms=hot, cold_ms=cold, ms_append=ms_append, out=out,
                 stream_read_gbps=nbytes / (sr_ms * 1e-3) / 1e9,
                 device=dev_name, width=dev.max_blocks, launches=dev.launches,
-                read_bytes=read_bytes)
+                read_bytes=read_bytes, swap_ms=swap, swap_bytes=swap_bytes, swap_blocks=nsw)
 
 
 def main(argv=None):
@@ -373,6 +401,12 @@ def main(argv=None):
         "decode_us": {"hot": float(np.median(hot)) * 1e3, "hot_runs": [float(x) * 1e3 for x in hot],
                       "cold_median": float(np.median(cold)) * 1e3, "cold_min": float(cold.min()) * 1e3},
         "cache_append_us": g["ms_append"] * 1e3,
+        "swap": {  # pa_swap_blocks to / from a pinned host pool (host link: PCIe 5.0 x16, 64 GB/s each way)
+            "blocks": g["swap_blocks"], "bytes": g["swap_bytes"],
+            "out_gbps": g["swap_bytes"] / (g["swap_ms"]["out"] * 1e-3) / 1e9,
+            "in_gbps": g["swap_bytes"] / (g["swap_ms"]["in"] * 1e-3) / 1e9,
+            "host_link_peak_gbps": HOST_LINK_GBPS,
+        },
         "stream_read_gbps_same_bytes": g["stream_read_gbps"],
         "kv_tokens_per_s": float(w.seq_lens.sum()) / t_dec,
         "roofline": {

@@ -167,6 +167,28 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
+ * Copy whole blocks from one pool to another with the same block shape:
+ * the data movement of swapping a preempted request's blocks out to a host
+ * pool and back in (the MCQ page names preemption among what paging makes
+ * easy; pa_alloc_move gives the pairs).
+ *
+ *   src_k, src_v   source pool ([src_num_blocks] blocks, the layout above)
+ *   dst_k, dst_v   destination pool ([dst_num_blocks] blocks)
+ *   pairs          int32 [num_pairs][2] = (source block, destination block);
+ *                  a pair with a block out of range is skipped; no
+ *                  destination block may appear twice.
+ * Each of the five buffers is device memory or pinned host memory
+ * (hipHostMalloc, e.g. a torch tensor made with pin_memory=True), which the
+ * kernel reads or writes over the host link; pageable host memory is
+ * rejected with PA_ERR_INVALID_ARG before anything is enqueued.  A host
+ * destination holds the data once the stream has reached the copy.
+ * ------------------------------------------------------------------------ */
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks, void* dst_k,
+                         void* dst_v, int32_t dst_num_blocks, const int32_t* pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
  * Shared-prefix decode: the same result as pa_decode (same arguments, same
  * output, same handling of empty rows and bad tables), computed so that
  * the keys and values of blocks that several requests share are read once
@@ -324,6 +346,21 @@ pa_status pa_alloc_table(const pa_allocator* a, int64_t seq, int32_t* out, int32
 pa_status pa_alloc_batch_tables(const pa_allocator* a, const int64_t* seqs, int32_t n_seqs,
                                 int32_t* tables_out, int32_t width, int32_t pad,
                                 int32_t* seq_lens_out);
+/* Move sequences from allocator `from` to allocator `to` (same block size):
+ * swap-out (device pool -> host pool) and swap-in (back).  Every distinct
+ * block the listed sequences hold in `from` takes one fresh block of `to`,
+ * in order of first appearance (sequences in the given order, each table
+ * from logical block 0), so blocks the moved sequences share stay shared;
+ * host pairs_out [2 * cap] receives (from block, to block) for each, *n_pairs
+ * their count — the copies the caller makes with pa_swap_blocks before it
+ * reuses the freed blocks.  In `from` the sequences are then freed as by
+ * pa_alloc_free in the given order (a block another sequence still holds
+ * stays).  All or nothing: PA_ERR_NOT_FOUND (a sequence not in `from`),
+ * PA_ERR_EXISTS (already in `to`), PA_ERR_OOM (too few free blocks in `to`),
+ * PA_ERR_INVALID_ARG (a sequence listed twice, different block sizes, or
+ * cap too small — then *n_pairs is set to the room needed) change nothing. */
+pa_status pa_alloc_move(pa_allocator* from, pa_allocator* to, const int64_t* seqs, int32_t n_seqs,
+                        int32_t* pairs_out, int32_t cap, int32_t* n_pairs);
 /* Reference count of a block (-1 if out of range). */
 int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);
 /* Free queue in order, head first: up to `cap` ids into host `out`, *n = its length. */

@@ -124,6 +124,42 @@ class BlockAllocatorModel:
                 self.free.append(phys)
         del self.lens[seq]
 
+    def move_to(self, other: "BlockAllocatorModel", seqs: Sequence[int]) -> List[Tuple[int, int]]:
+        """Swap the given sequences out to (or back in from) another pool.
+
+        The MCQ page lists easy preemption among what paging gives; it says no
+        more.  Reading: each distinct block the sequences hold here is given
+        one fresh block there, in order of first appearance, so what they
+        share stays shared; the sequences are then freed here in the given
+        order.  Returns the (here, there) block pairs whose contents must be
+        copied.  All or nothing.
+        """
+        seqs = list(seqs)
+        if len(set(seqs)) != len(seqs) or other.block_size != self.block_size:
+            raise ValueError("bad move")
+        for s in seqs:
+            if s not in self.tables:
+                raise UnknownSequence(s)
+            if s in other.tables:
+                raise ValueError(f"sequence {s} exists there")
+        order: List[int] = []
+        for s in seqs:
+            for b in self.tables[s]:
+                if b not in order:
+                    order.append(b)
+        if len(order) > len(other.free):
+            raise OutOfBlocks(seqs)
+        there = {b: other.free.popleft() for b in order}
+        for b in order:
+            other.ref[there[b]] = 0
+        for s in seqs:
+            other.tables[s] = [there[b] for b in self.tables[s]]
+            other.lens[s] = self.lens[s]
+            for b in other.tables[s]:
+                other.ref[b] += 1
+            self.free_seq(s)
+        return [(b, there[b]) for b in order]
+
     # -- accounting (pages' worked example: slots held / used / wasted) ----
     def held_slots(self, seqs: Optional[Sequence[int]] = None) -> int:
         """Slots of the distinct physical blocks the given requests hold."""

@@ -31,7 +31,7 @@ __all__ = [
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
     "new_workspace", "SharedPrefixPlan", "plan_shared_prefix", "decode_shared_prefix",
     "decode_shared_prefix_workspace_bytes", "shared_prefix_max_group", "simulate_memory", "PA_MEM_CONTIGUOUS",
-    "PA_MEM_PAGED",
+    "PA_MEM_PAGED", "swap_blocks",
 ]
 
 
@@ -314,6 +314,26 @@ def simulate_memory(arrival, prompt, reply, capacity_slots: int, scheme: int, pa
     return {name: int(getattr(st, name)) for name, _ in MemStats._fields_}
 
 
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:
+    """Copy blocks pairs[i, 0] of (src_k, src_v) to blocks pairs[i, 1] of
+    (dst_k, dst_v); pools on the device or in pinned host memory."""
+    nb_s, hkv, bs, d = _pool_dims(src_k, src_v)
+    nb_d, hkv2, bs2, d2 = _pool_dims(dst_k, dst_v)
+    if (hkv, bs, d) != (hkv2, bs2, d2) or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools differ in block shape or dtype")
+    if pairs.dtype != _torch().int32 or (pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2)):
+        raise ValueError("pairs must be int32 [n, 2]")
+    n = pairs.shape[0] if pairs.numel() else 0
+    if n == 0:
+        return
+    for name, t in (("src_k", src_k), ("src_v", src_v), ("dst_k", dst_k), ("dst_v", dst_v), ("pairs", pairs)):
+        if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a contiguous device or pinned host tensor")
+    check(lib().pa_swap_blocks(src_k.data_ptr(), src_v.data_ptr(), nb_s, dst_k.data_ptr(), dst_v.data_ptr(), nb_d,
+                               pairs.data_ptr(), n, hkv, d, bs, _dtype_code(src_k.dtype), _stream_ptr(stream)),
+          "pa_swap_blocks")
+
+
 def stream_read(buf, sink, workgroups: int = 0, stream=None) -> None:
     """Measurement helper: read every byte of device tensor ``buf`` once (pa_bench_stream_read)."""
     if sink.dtype != _torch().int32 or sink.numel() < 1:
@@ -387,6 +407,17 @@ class Allocator:
                                               tables.ctypes.data_as(P_I32), width, pad, lens.ctypes.data_as(P_I32)),
               "pa_alloc_batch_tables")
         return tables, lens
+
+    def move(self, to: "Allocator", seqs: Sequence[int]):
+        """Move sequences to allocator ``to`` (swap out / in); returns the
+        (from block, to block) copy pairs as int32 [n, 2]."""
+        seqs = np.ascontiguousarray(np.asarray(list(seqs), dtype=np.int64))
+        n = ctypes.c_int32(0)
+        cap = max(1, sum(len(self.table(int(s))[0]) for s in seqs)) if len(seqs) else 1
+        pairs = np.zeros(2 * cap, dtype=np.int32)
+        check(self._lib.pa_alloc_move(self._h, to._h, seqs.ctypes.data_as(P_I64), len(seqs),
+                                      pairs.ctypes.data_as(P_I32), cap, ctypes.byref(n)), "pa_alloc_move")
+        return pairs[:2 * n.value].reshape(n.value, 2).copy()
 
     def refcount(self, block: int) -> int:
         return int(self._lib.pa_alloc_refcount(self._h, block))

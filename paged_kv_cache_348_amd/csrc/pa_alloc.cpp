@@ -203,3 +203,69 @@ extern "C" pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int
 extern "C" int32_t pa_alloc_num_free(const pa_allocator* a) {
     return a ? static_cast<int32_t>(a->free_q.size()) : -1;
 }
+
+// Move sequences between two allocators (device pool <-> host pool for
+// preemption by swapping; the MCQ page lists preemption among the things
+// paging makes easy).  Every distinct block the moved sequences hold in
+// `from` gets one fresh block in `to`, in order of first appearance (the
+// sequences in the given order, each table from logical block 0), so
+// sharing among the moved sequences is kept; the pairs (from block, to
+// block) are what the caller copies.  In `from` the moved sequences are
+// freed as pa_alloc_free would, in the given order: a block also held by a
+// sequence that stays keeps its data there.
+extern "C" pa_status pa_alloc_move(pa_allocator* from, pa_allocator* to, const int64_t* seqs, int32_t n_seqs,
+                                   int32_t* pairs_out, int32_t cap, int32_t* n_pairs) {
+    if (!from || !to || from == to || n_seqs < 0 || cap < 0 || !n_pairs || (n_seqs > 0 && !seqs) ||
+        (cap > 0 && !pairs_out))
+        return PA_ERR_INVALID_ARG;
+    if (from->block_size != to->block_size) return PA_ERR_INVALID_ARG;
+    std::unordered_map<int64_t, int> seen_seq;
+    std::unordered_map<int32_t, int32_t> map;  // from block -> index of first appearance
+    std::vector<int32_t> order;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+        if (seen_seq.count(seqs[i])) return PA_ERR_INVALID_ARG;  // a sequence listed twice
+        seen_seq[seqs[i]] = 1;
+        auto it = from->seqs.find(seqs[i]);
+        if (it == from->seqs.end()) return PA_ERR_NOT_FOUND;
+        if (to->seqs.count(seqs[i])) return PA_ERR_EXISTS;
+        for (int32_t b : it->second.table) {
+            if (!map.count(b)) {
+                map[b] = static_cast<int32_t>(order.size());
+                order.push_back(b);
+            }
+        }
+    }
+    const int64_t need = static_cast<int64_t>(order.size());
+    if (need > cap) {
+        *n_pairs = static_cast<int32_t>(need);  // the room the pairs need; nothing changed
+        return PA_ERR_INVALID_ARG;
+    }
+    if (need > static_cast<int64_t>(to->free_q.size())) return PA_ERR_OOM;
+    // destination blocks, one per distinct source block
+    std::vector<int32_t> dst(order.size());
+    for (size_t k = 0; k < order.size(); ++k) {
+        dst[k] = to->free_q.front();
+        to->free_q.pop_front();
+        to->ref[dst[k]] = 0;
+        pairs_out[2 * k] = order[k];
+        pairs_out[2 * k + 1] = dst[k];
+    }
+    for (int32_t i = 0; i < n_seqs; ++i) {
+        auto it = from->seqs.find(seqs[i]);
+        pa_allocator::Seq moved;
+        moved.len = it->second.len;
+        moved.table.reserve(it->second.table.size());
+        for (int32_t b : it->second.table) {
+            const int32_t d = dst[map[b]];
+            to->ref[d] += 1;
+            moved.table.push_back(d);
+        }
+        to->seqs.emplace(seqs[i], std::move(moved));
+        for (int32_t b : it->second.table) {
+            if (--from->ref[b] == 0) from->free_q.push_back(b);
+        }
+        from->seqs.erase(it);
+    }
+    *n_pairs = static_cast<int32_t>(order.size());
+    return PA_OK;
+}

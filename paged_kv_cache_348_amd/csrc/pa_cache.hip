@@ -70,10 +70,47 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc,
     }
 }
 
+// Whole-block copies from one pool to another of the same block shape (a
+// device pool and a pinned host pool when a request is swapped out or back
+// in).  Pair p copies block pairs[p][0] of the source to block pairs[p][1]
+// of the destination, keys and values; workgroup row y takes pairs y,
+// y + gridDim.y, ...
+__global__ __launch_bounds__(256) void swap_blocks_kernel(const char* __restrict__ sk, const char* __restrict__ sv,
+                                                          char* __restrict__ dk, char* __restrict__ dv,
+                                                          const int32_t* __restrict__ pairs, int num_pairs,
+                                                          int64_t block_bytes, int src_blocks, int dst_blocks) {
+    const int64_t nvec = block_bytes / 16;
+    for (int pi = blockIdx.y; pi < num_pairs; pi += gridDim.y) {
+        const int32_t src = pairs[2 * pi];
+        const int32_t dst = pairs[2 * pi + 1];
+        if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) continue;
+        const int64_t so = (int64_t)src * block_bytes, dO = (int64_t)dst * block_bytes;
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
+             i += (int64_t)gridDim.x * blockDim.x) {
+            st16(dk + dO + i * 16, ld16(sk + so + i * 16));
+            st16(dv + dO + i * 16, ld16(sv + so + i * 16));
+        }
+    }
+}
+
 }  // namespace pa
 
 namespace {
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Address a kernel can use for p: device memory as is, pinned host memory
+// (hipHostMalloc) through its device mapping; anything else (pageable host
+// memory, unknown pointers) gives nullptr.
+inline const void* device_view(const void* p) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error a failed query leaves
+        return nullptr;
+    }
+    if (at.type == hipMemoryTypeDevice) return p;
+    if (at.type == hipMemoryTypeHost && at.devicePointer) return at.devicePointer;
+    return nullptr;
+}
 
 inline pa_status check_pool(int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                             pa_dtype dtype) {
@@ -131,5 +168,35 @@ extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t*
     hipLaunchKernelGGL(pa::copy_blocks_kernel, dim3((unsigned)gx, (unsigned)num_pairs), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), reinterpret_cast<char*>(k_cache),
                        reinterpret_cast<char*>(v_cache), pairs, block_bytes, num_blocks);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+extern "C" pa_status pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks, void* dst_k,
+                                    void* dst_v, int32_t dst_num_blocks, const int32_t* pairs, int32_t num_pairs,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                                    void* stream) {
+    if (num_pairs < 0 || src_num_blocks < 0) return PA_ERR_INVALID_ARG;
+    pa_status st = check_pool(num_kv_heads, head_dim, block_size, dst_num_blocks, dtype);
+    if (st != PA_OK) return st;
+    if (num_pairs == 0) return PA_OK;
+    if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PA_ERR_INVALID_ARG;
+    if (!al16(src_k) || !al16(src_v) || !al16(dst_k) || !al16(dst_v) || (reinterpret_cast<uintptr_t>(pairs) & 3u))
+        return PA_ERR_INVALID_ARG;
+    const void* sk = device_view(src_k);
+    const void* sv = device_view(src_v);
+    const void* dk = device_view(dst_k);
+    const void* dv = device_view(dst_v);
+    const void* pp = device_view(pairs);
+    if (!sk || !sv || !dk || !dv || !pp) return PA_ERR_INVALID_ARG;  // pageable or unknown memory
+    const int es = dtype == PA_BF16 ? 2 : 4;
+    const int64_t block_bytes = (int64_t)num_kv_heads * head_dim * block_size * es;
+    int64_t gx = (block_bytes / 16 + 255) / 256;
+    if (gx > 64) gx = 64;
+    const int gy = num_pairs < 65535 ? num_pairs : 65535;
+    hipLaunchKernelGGL(pa::swap_blocks_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const char*>(sk),
+                       reinterpret_cast<const char*>(sv), reinterpret_cast<char*>(const_cast<void*>(dk)),
+                       reinterpret_cast<char*>(const_cast<void*>(dv)), reinterpret_cast<const int32_t*>(pp), num_pairs,
+                       block_bytes, src_num_blocks, dst_num_blocks);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
