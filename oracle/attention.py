@@ -89,6 +89,35 @@ def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, rows
     return out
 
 
+def paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale: float,
+                  rows=None) -> np.ndarray:
+    """Causal multi-token query (prefill, chunked prefill, verification): [T, Hq, D] float64.
+
+    The cache grows by the tokens a step adds ("Paged attention in LLMs",
+    "The cache being stored"), so a request with ``seq_lens[b]`` = L cached
+    tokens whose last M are new has query rows ``query_start[b] ..
+    query_start[b+1] - 1``; query token i sits at position L - M + i and, as
+    in any autoregressive model, sees the keys at positions up to its own.
+    Each row is therefore exactly the decode of that token over the first
+    L - M + i + 1 positions.  Only the requests in ``rows`` are computed when
+    given; the others' rows stay zero.
+    """
+    qd = widen(q)
+    T, Hq, D = qd.shape
+    out = np.zeros((T, Hq, D))
+    B = len(seq_lens)
+    for b in (range(B) if rows is None else rows):
+        t0, t1 = int(query_start[b]), int(query_start[b + 1])
+        L, M = int(seq_lens[b]), t1 - t0
+        if M == 0:
+            continue
+        K, V = gather_sequence(k_cache, v_cache, block_tables[b], L)
+        for i in range(M):
+            p = L - M + i
+            out[t0 + i] = dense_attention(qd[t0 + i], K[: p + 1], V[: p + 1], scale)
+    return out
+
+
 def paged_decode_loops(q, k_cache, v_cache, block_tables, seq_lens, scale: float) -> np.ndarray:
     """The same result with plain Python loops and no array arithmetic (tiny inputs only)."""
     import math

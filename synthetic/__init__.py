@@ -13,4 +13,5 @@ from .workloads import (  # noqa: F401
     f32_from_bf16_bits,
     MemoryTrace,
     memory_trace,
+    multi_query,
 )

@@ -401,3 +401,17 @@ def memory_trace(seed: int = 0, requests: int = 2000, mean_gap: float = 0.5, pro
     prompt = g.integers(prompt_lo, prompt_hi + 1, size=requests)
     reply = np.minimum(np.floor(g.exponential(reply_mean, size=requests)), max_reply)
     return MemoryTrace(arrival.astype(np.int32), prompt.astype(np.int32), reply.astype(np.int32), max_reply)
+
+
+def multi_query(w: Workload, query_lens, seed: int = 0):
+    """Queries for a multi-token step over workload ``w``: request b's last
+    ``query_lens[b]`` tokens (positions L_b - M_b .. L_b - 1, whose keys and
+    values the workload already holds) get fresh N(0, 1) queries.  Returns
+    (q [T, Hq, D] in the workload dtype, query_start int32 [B + 1])."""
+    m = np.asarray(query_lens, dtype=np.int64)
+    assert m.shape == (w.batch,)
+    qs = np.zeros(w.batch + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(m)
+    g = _rng(seed, w.config_id, S_Q, 1)
+    q = g.standard_normal((int(qs[-1]), w.num_q_heads, w.head_dim), dtype=np.float32)
+    return (bf16_bits_from_f32(q) if w.dtype == "bf16" else q), qs
