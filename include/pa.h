@@ -167,6 +167,37 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
+ * Multi-token query over the paged cache: prefill, chunked prefill and
+ * speculative verification.  Request b has L_b = seq_lens[b] tokens in the
+ * cache, the last M_b of them new (their keys and values already written
+ * with pa_cache_write, as the cache grows by what a step adds: "Paged
+ * attention in LLMs", "The cache being stored").  Its M_b query tokens are
+ * rows query_start[b] .. query_start[b+1] - 1 of q; query token i sits at
+ * position p = L_b - M_b + i and attends causally, to positions 0 .. p:
+ *   out[t][h] = softmax_k(scale * q[t][h] . K[k][g]) . V[k][g],  k in [0, p]
+ * with g = h / (num_q_heads / num_kv_heads) and K, V read through the block
+ * table as for pa_decode (MCQ page, code sketch).
+ *
+ *   q            device, [num_query_tokens][num_q_heads][head_dim], dtype
+ *   query_start  device, int32 [num_seqs + 1], non-decreasing from 0 to
+ *                num_query_tokens (M_b = query_start[b+1] - query_start[b],
+ *                0 allowed)
+ *   out          device, [num_query_tokens][num_q_heads][head_dim], dtype
+ *   max_query_len  >= every M_b (sizes the launch)
+ *   num_q_heads / num_kv_heads <= 16; the other arguments as for pa_decode.
+ * Error rows: a request with M_b > L_b, M_b > max_query_len, or L_b longer
+ * than its table holds gets NaN in all its rows; a table entry outside
+ * [0, num_blocks) among a query tile's keys gives NaN rows for that tile; a
+ * request whose query_start pair is out of order or outside
+ * [0, num_query_tokens] writes nothing.  Nothing faults.
+ * ------------------------------------------------------------------------ */
+pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     const int32_t* seq_lens, const int32_t* query_start, int32_t num_kv_heads, float scale,
+                     void* out, void* stream, int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                     pa_dtype dtype, int32_t max_query_len);
+
+/* ------------------------------------------------------------------------
  * Copy whole blocks from one pool to another with the same block shape:
  * the data movement of swapping a preempted request's blocks out to a host
  * pool and back in (the MCQ page names preemption among what paging makes

@@ -31,7 +31,7 @@ __all__ = [
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
     "new_workspace", "SharedPrefixPlan", "plan_shared_prefix", "decode_shared_prefix",
     "decode_shared_prefix_workspace_bytes", "shared_prefix_max_group", "simulate_memory", "PA_MEM_CONTIGUOUS",
-    "PA_MEM_PAGED", "swap_blocks",
+    "PA_MEM_PAGED", "swap_blocks", "prefill",
 ]
 
 
@@ -312,6 +312,37 @@ def simulate_memory(arrival, prompt, reply, capacity_slots: int, scheme: int, pa
                                    arrs[2].ctypes.data_as(P_I32), n, int(capacity_slots), scheme, param,
                                    ctypes.byref(st)), "pa_simulate_memory")
     return {name: int(getattr(st, name)) for name, _ in MemStats._fields_}
+
+
+def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_heads: int, scale: float,
+            max_query_len: int, out=None, stream=None):
+    """Causal multi-token query over the paged cache (pa_prefill): q [T, Hq, D]
+    holds each request's new tokens, rows query_start[b] .. query_start[b+1]-1;
+    the last M_b of its seq_lens[b] cached tokens are those tokens.  Returns out [T, Hq, D]."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    if hkv != num_kv_heads:
+        raise ValueError("num_kv_heads does not match the cache")
+    T, hq, dq = q.shape
+    if dq != d or q.dtype != k_cache.dtype:
+        raise ValueError("q must be [T, Hq, head_dim] in the cache dtype")
+    B = seq_lens.numel()
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if seq_lens.dtype != torch.int32 or query_start.dtype != torch.int32 or query_start.numel() != B + 1:
+        raise ValueError("seq_lens must be int32 [B] and query_start int32 [B + 1]")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if B == 0 or T == 0:
+        return out
+    check(lib().pa_prefill(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
+                           _dev(query_start, "query_start"), hkv, float(scale), _dev(out, "out"), _stream_ptr(stream),
+                           B, T, hq, d, bs, nb, block_tables.shape[1], _dtype_code(q.dtype), int(max_query_len)),
+          "pa_prefill")
+    return out
 
 
 def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:

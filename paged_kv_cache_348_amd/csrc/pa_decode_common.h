@@ -181,13 +181,18 @@ __device__ __forceinline__ float wave_sum16(float x) { return pair32_sum(pair16_
 // online-softmax update and the PV accumulation.  Tokens at or past L are
 // masked: their scores become -inf and their values are zeroed, since a
 // stale or NaN value times a zero weight would still poison the sum.
-template <bool BF16, int D, int BS>
+// CAUSAL: each lane's column has its own key limit Lcol <= L (a query token
+// sees the keys up to its own position); Lmin is the smallest limit of the
+// wave's columns, so steps wholly below it skip the masking.  Values are
+// still zeroed only at or past L (everything below L is stored data).
+template <bool BF16, int D, int BS, bool CAUSAL = false>
 __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
                                              const u32x4 (&qr)[DecodeCfg<BF16, D, BS>::NKC], float& m_run,
                                              float& l_run, f32x4 (&acc)[DecodeCfg<BF16, D, BS>::NV], int tok0,
-                                             int L, int j, float scale_log2) {
+                                             int L, int j, float scale_log2, int Lcol = 0, int Lmin = 0) {
     using C = DecodeCfg<BF16, D, BS>;
-    const bool tail = tok0 + C::STEP > L;
+    const int Ls = CAUSAL ? Lcol : L;  // score limit of this lane's column
+    const bool tail = tok0 + C::STEP > (CAUSAL ? Lmin : L);
     if constexpr (BF16) {
         // ---- scores: two 16-token tiles (rows as in issue_step_e); lane (n, j)
         // receives rows 4j+i of tile a and of tile b
@@ -216,7 +221,7 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
             };
             uint32_t keep[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] = (tok(e) < L) ? s[e] : -INFINITY;
+            for (int e = 0; e < 8; ++e) s[e] = (tok(e) < Ls) ? s[e] : -INFINITY;
 #pragma unroll
             for (int w = 0; w < 4; ++w)
                 keep[w] = ((tok(2 * w) < L) ? 0x0000ffffu : 0u) | ((tok(2 * w + 1) < L) ? 0xffff0000u : 0u);
@@ -267,7 +272,7 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
         if (tail) {
             const int base = tok0 + 4 * j;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[i] = (base + i < L) ? s[i] : -INFINITY;
+            for (int i = 0; i < 4; ++i) s[i] = (base + i < Ls) ? s[i] : -INFINITY;
 #pragma unroll
             for (int c = 0; c < C::NV; ++c)
                 cur.v[c] = u32x4{base + 0 < L ? cur.v[c][0] : 0u, base + 1 < L ? cur.v[c][1] : 0u,

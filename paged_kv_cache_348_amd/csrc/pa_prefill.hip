@@ -1,0 +1,242 @@
+// Multi-token query over the paged cache (pa_prefill in include/pa.h):
+// prefill, chunked prefill and speculative verification all attend a run of
+// new query tokens of a request to its cached keys and values with a causal
+// mask.  The new tokens' keys and values are in the cache already (written
+// with pa_cache_write, as the cache grows by the tokens a step adds: "Paged
+// attention in LLMs", "The cache being stored"); query token i of a request
+// with L cached tokens and M new ones sits at position L - M + i and sees the
+// keys at positions 0 .. L - M + i.  The attention is the standard scaled
+// dot-product over those keys, reached through the block table (MCQ page,
+// code sketch: the lookup inside the tile loop).
+//
+// One wave per (kv-head, tile of query tokens, request).  The tile's query
+// columns are (token, head) pairs, token-major: QT tokens x G heads, up to
+// 64 columns in 16-column matrix-core tiles (32 for float32 with head dim
+// 128).  The wave streams the request's keys and values from position 0 to
+// its last token's position once for all columns — the same step loop as the
+// decode kernels — and each lane masks the keys past its own column's
+// position.  Every column sees key 0, so no running maximum stays -inf.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "pa.h"
+#include "pa_decode_common.h"
+
+namespace pa {
+
+template <bool BF16, int D>
+__device__ __forceinline__ void store_row(void* __restrict__ out_, int64_t row, const f32x4 (&acc)[D / 16], float inv,
+                                          int j) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        const int d0 = 16 * c + 4 * j;
+        if constexpr (BF16) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv);
+            w.y = pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out_) + row * D + d0) = w;
+        } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out_) + row * D + d0) = acc[c] * inv;
+        }
+    }
+}
+
+template <bool BF16, int D, int BS, int NCT>
+__global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_, const void* __restrict__ kc_,
+                                                     const void* __restrict__ vc_, const int32_t* __restrict__ tables,
+                                                     const int32_t* __restrict__ lens,
+                                                     const int32_t* __restrict__ q_start, void* __restrict__ out_,
+                                                     int T, int Hq, int Hkv, int G, int QT, int max_q,
+                                                     int max_blocks, int num_blocks, float scale_log2) {
+    using C = DecodeCfg<BF16, D, BS>;
+    const int g = blockIdx.x;
+    const int qt = blockIdx.y;
+    const int b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    const int t0 = q_start[b];
+    const int t1 = q_start[b + 1];
+    if (t0 < 0 || t1 > T || t1 < t0) return;  // malformed query offsets: the request writes nothing
+    const int M = t1 - t0;
+    const int L = lens[b];
+    if (M > max_q || M > L || (int64_t)L > (int64_t)max_blocks * BS) {
+        // more query tokens than the launch bound or than cached tokens, or a
+        // length the table cannot hold: tile 0 writes NaN in all the request's rows
+        if (qt != 0) return;
+        for (int64_t i = lane; i < (int64_t)M * G * D; i += 64) {
+            const int c = (int)(i / D);
+            const int64_t row = (int64_t)(t0 + c / G) * Hq + g * G + c % G;
+            if constexpr (BF16)
+                reinterpret_cast<uint16_t*>(out_)[row * D + i % D] = (uint16_t)bf16_bits_rne(__builtin_nanf(""));
+            else
+                reinterpret_cast<float*>(out_)[row * D + i % D] = __builtin_nanf("");
+        }
+        return;
+    }
+    const int q0 = qt * QT;
+    if (q0 >= M) return;
+    const int nq = min(QT, M - q0);  // query tokens of this tile
+    const int ncol = nq * G;
+    const int pos0 = L - M + q0;  // position of the tile's first query token
+    const int Lend = pos0 + nq;   // keys the tile needs: [0, Lend)
+
+    typename C::QRegs qr[NCT];
+    int Lcol[NCT];
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) {
+        const int c = min(16 * t + n, ncol - 1);  // padding columns repeat the last one and are never stored
+        const char* qp = reinterpret_cast<const char*>(q_) + ((int64_t)(t0 + q0 + c / G) * Hq + g * G + c % G) * D * C::ES;
+#pragma unroll
+        for (int k = 0; k < C::NKC; ++k) qr[t][k] = ld16(qp + (int64_t)(4 * k + j) * 16);
+        Lcol[t] = pos0 + c / G + 1;
+    }
+    RunState<BF16, D, BS> S[NCT];
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) run_init(S[t]);
+
+    const int64_t blk_bytes = (int64_t)Hkv * C::TILE * C::ES;
+    const char* kbase = reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES;
+    const char* vbase = reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES;
+    const int32_t* trow = tables + (int64_t)b * max_blocks;
+    bool bad = false;
+    for (int ctok = 0; ctok < Lend; ctok += kTableChunk * BS) {
+        const int cend = min(ctok + kTableChunk * BS, Lend);
+        const int blk0 = ctok / BS;
+        const int nblk = (cend - 1) / BS - blk0 + 1;
+        const int32_t ent = (lane < nblk) ? trow[blk0 + lane] : 0;
+        if (__any(lane < nblk && (ent < 0 || ent >= num_blocks))) {
+            bad = true;
+            break;
+        }
+        const int nst = (cend - ctok + C::STEP - 1) / C::STEP;
+        StepRegs<BF16, D, BS> cur;
+        issue_step<BF16, D, BS>(cur, kbase, vbase, blk_bytes, ent, blk0, nblk, ctok, Lend, n, j);
+        int tok0 = ctok;
+        for (int st = 0; st + 1 < nst; ++st, tok0 += C::STEP) {
+            StepRegs<BF16, D, BS> nxt;
+            issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, Lend, n, j);
+            __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the compute
+#pragma unroll
+            for (int t = 0; t < NCT; ++t)
+                compute_step<BF16, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, tok0, Lend, j, scale_log2,
+                                                Lcol[t], pos0 + (16 * t) / G + 1);
+            cur = nxt;
+        }
+#pragma unroll
+        for (int t = 0; t < NCT; ++t)
+            compute_step<BF16, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, tok0, Lend, j, scale_log2,
+                                            Lcol[t], pos0 + (16 * t) / G + 1);
+    }
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) {
+        const int c = 16 * t + n;
+        if (c < ncol) {
+            const int64_t row = (int64_t)(t0 + q0 + c / G) * Hq + g * G + c % G;
+            store_row<BF16, D>(out_, row, S[t].acc, bad ? __builtin_nanf("") : 1.0f / S[t].l, j);
+        }
+    }
+}
+
+}  // namespace pa
+
+// ---------------------------------------------------------------------------- host side
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Query columns one wave holds: four 16-column tiles, two for float32 with
+// head dim 128 (four would not fit the register file).
+constexpr int max_columns(bool bf16, int head_dim) { return (!bf16 && head_dim == 128) ? 32 : 64; }
+
+struct PrefillLaunch {
+    const void *q, *kc, *vc;
+    const int32_t *tables, *lens, *qs;
+    void* out;
+    int T, B, Hq, Hkv, G, QT, max_q, n_tiles, max_blocks, num_blocks;
+    float sl2;
+    hipStream_t s;
+};
+
+template <bool BF16, int D, int BS, int NCT>
+hipError_t launch_prefill(const PrefillLaunch& a) {
+    hipLaunchKernelGGL((pa::prefill_kernel<BF16, D, BS, NCT>), dim3((unsigned)a.Hkv, (unsigned)a.n_tiles, (unsigned)a.B),
+                       dim3(64), 0, a.s, a.q, a.kc, a.vc, a.tables, a.lens, a.qs, a.out, a.T, a.Hq, a.Hkv, a.G, a.QT,
+                       a.max_q, a.max_blocks, a.num_blocks, a.sl2);
+    return hipGetLastError();
+}
+
+template <bool BF16, int D, int BS>
+hipError_t prefill_cols(int cols, const PrefillLaunch& a) {
+    if (cols <= 16) return launch_prefill<BF16, D, BS, 1>(a);
+    if (cols <= 32 || max_columns(BF16, D) == 32) return launch_prefill<BF16, D, BS, 2>(a);
+    return launch_prefill<BF16, D, BS, max_columns(BF16, D) / 16>(a);
+}
+
+template <bool BF16, int D>
+hipError_t prefill_bs(int BS, int cols, const PrefillLaunch& a) {
+    switch (BS) {
+        case 8: return prefill_cols<BF16, D, 8>(cols, a);
+        case 16: return prefill_cols<BF16, D, 16>(cols, a);
+        default: return prefill_cols<BF16, D, 32>(cols, a);
+    }
+}
+
+}  // namespace
+
+extern "C" pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                const int32_t* seq_lens, const int32_t* query_start, int32_t num_kv_heads, float scale,
+                                void* out, void* stream, int32_t num_seqs, int32_t num_query_tokens,
+                                int32_t num_q_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, pa_dtype dtype, int32_t max_query_len) {
+    if (num_seqs < 0 || num_query_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 ||
+        max_blocks_per_seq < 0 || max_query_len < 0 || !std::isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != 8 && block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    const int G = num_q_heads / num_kv_heads;
+    const int maxc = max_columns(dtype == PA_BF16, head_dim);
+    if (G > 16) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start || !out) return PA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(query_start) & 3u))
+        return PA_ERR_INVALID_ARG;
+    PrefillLaunch a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.tables = block_tables;
+    a.lens = seq_lens;
+    a.qs = query_start;
+    a.out = out;
+    a.T = num_query_tokens;
+    a.B = num_seqs;
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.G = G;
+    a.QT = maxc / G;  // query tokens per wave
+    a.max_q = max_query_len;
+    const int qt_used = std::min(a.QT, (int)max_query_len);
+    a.n_tiles = (max_query_len + a.QT - 1) / a.QT;
+    if (a.n_tiles > 65535) return PA_ERR_UNSUPPORTED;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.sl2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+    a.s = reinterpret_cast<hipStream_t>(stream);
+    const int cols = qt_used * G;
+    hipError_t e;
+    if (dtype == PA_BF16)
+        e = head_dim == 128 ? prefill_bs<true, 128>(block_size, cols, a) : prefill_bs<true, 64>(block_size, cols, a);
+    else
+        e = head_dim == 128 ? prefill_bs<false, 128>(block_size, cols, a) : prefill_bs<false, 64>(block_size, cols, a);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}

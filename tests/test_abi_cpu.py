@@ -407,3 +407,33 @@ def test_plan_rejects_bad_arguments():
     assert call(mg=0) == pa.PA_ERR_INVALID_ARG
     assert call(mins=0) == pa.PA_ERR_INVALID_ARG
     assert call(groups=None) == pa.PA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- multi-token query (host side)
+def prefill_call(**kw):
+    a = dict(q=fake(), kc=fake(), vc=fake(), bt=fake(), sl=fake(), qs=fake(), hkv=8, scale=0.1, out=fake(),
+             stream=None, B=4, T=16, hq=32, d=128, bs=16, nb=100, mb=8, dt=1, mq=4)
+    a.update(kw)
+    return _l().pa_prefill(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["qs"], a["hkv"], a["scale"], a["out"],
+                           a["stream"], a["B"], a["T"], a["hq"], a["d"], a["bs"], a["nb"], a["mb"], a["dt"], a["mq"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(hq=30), pa.PA_ERR_INVALID_ARG),
+    (dict(hq=8 * 17), pa.PA_ERR_UNSUPPORTED),
+    (dict(d=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=24), pa.PA_ERR_UNSUPPORTED),
+    (dict(dt=7), pa.PA_ERR_UNSUPPORTED),
+    (dict(B=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(T=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(mq=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), pa.PA_ERR_INVALID_ARG),
+    (dict(qs=None), pa.PA_ERR_INVALID_ARG),
+    (dict(out=fake(0x10008)), pa.PA_ERR_INVALID_ARG),
+    (dict(qs=fake(0x10002)), pa.PA_ERR_INVALID_ARG),
+    (dict(B=0, q=None, kc=None, vc=None, bt=None, sl=None, qs=None, out=None), pa.PA_OK),
+    (dict(T=0, q=None, out=None), pa.PA_OK),
+    (dict(mq=0), pa.PA_OK),
+])
+def test_prefill_rejects_bad_arguments(kw, expect):
+    assert prefill_call(**kw) == expect

@@ -1,0 +1,132 @@
+"""GPU parity of the causal multi-token query (pa_prefill) against the oracle.
+
+Verification-sized chunks (a few tokens), chunked prefill and full prefill,
+group sizes 1..16, head dims 64 and 128, every block size, float32 and
+bfloat16, several query tiles per request, keys spanning several table
+chunks, empty chunks, and the documented error rows (more new tokens than
+cached ones, more than the launch bound, a bad table entry) — within 1e-5
+(float32) / 2e-2 (bfloat16) of the float64 oracle, NaN only where promised.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_348_amd as pa  # noqa: E402
+from paged_kv_cache_348_amd.workload import build_device_batch, to_device  # noqa: E402
+import oracle.attention as oa  # noqa: E402
+from oracle.cache import replay  # noqa: E402
+from synthetic import multi_query  # noqa: E402
+from synthetic.workloads import custom  # noqa: E402
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(*a):
+    print("[gpu-prefill]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def run(w, dev, m, seed=1, max_q=None, tables=None, lens=None, qs_override=None):
+    q, qs = multi_query(w, m, seed=seed)
+    if qs_override is not None:
+        qs = qs_override
+    qd = to_device(q, w.dtype, "cuda")
+    out = pa.prefill(qd, dev.k_cache, dev.v_cache, dev.block_tables if tables is None else tables,
+                     dev.seq_lens if lens is None else lens, torch.from_numpy(qs).to("cuda"), w.num_kv_heads,
+                     w.scale, int(max(m)) if max_q is None else max_q)
+    torch.cuda.synchronize()
+    return q, qs, out.float().cpu().numpy().astype(np.float64)
+
+
+CASES = [
+    # (label, dtype, Hq, Hkv, D, bs, lens, query lens: 'L' = all, int = fixed, float = fraction)
+    ("verify-bf16-G4", "bf16", 32, 8, 128, 16, [40, 77, 5, 300, 1, 1100], 4),
+    ("verify-bf16-G8-bs32", "bf16", 64, 8, 128, 32, [33, 260, 700, 2], 7),
+    ("full-bf16-G4", "bf16", 32, 8, 128, 16, [40, 77, 5, 150, 1], "L"),
+    ("chunk-bf16-G8", "bf16", 64, 8, 128, 16, [90, 400, 33], 0.3),
+    ("chunk-bf16-G1-bs8", "bf16", 8, 8, 128, 8, [200, 130, 64], 0.7),
+    ("chunk-bf16-G16-D64", "bf16", 16, 1, 64, 32, [100, 17, 250], 0.5),
+    ("long-keys-bf16", "bf16", 32, 8, 128, 16, [5000, 2100], 16),
+    ("full-f32-G1-D64", "f32", 8, 8, 64, 16, [14, 60, 1, 33], "L"),
+    ("chunk-f32-G4-D128-bs8", "f32", 32, 8, 128, 8, [90, 41, 160], 20),
+    ("chunk-f32-G2-D128-bs32", "f32", 6, 3, 128, 32, [70, 129], 0.4),
+]
+
+
+def query_lens(lens, spec):
+    lens = np.asarray(lens, dtype=np.int64)
+    if spec == "L":
+        return lens.copy()
+    if isinstance(spec, float):
+        return np.maximum(1, (lens * spec).astype(np.int64))
+    return np.minimum(lens, spec)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(case):
+    label, dtype, hq, hkv, d, bs, lens, spec = case
+    w = custom(seed=len(label) + sum(lens), dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=bs, lens=lens)
+    m = query_lens(w.seq_lens, spec)
+    say(label, "L", list(w.seq_lens), "M", list(m))
+    pool, _, tables, _, _ = replay(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    q, qs, got = run(w, dev, m)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
+    assert not np.isnan(got).any()
+    err = float(np.abs(got - ref).max())
+    say(label, f"max abs err {err:.3e}")
+    assert err <= TOL[dtype], err
+
+
+def test_one_token_chunks_equal_the_decode_bitwise():
+    w = custom(seed=11, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+               lens=[40, 77, 5, 300, 1])
+    dev = build_device_batch(w)
+    dev.cache_append()
+    m = np.ones(w.batch, dtype=np.int64)
+    q, qs, got = run(w, dev, m)
+    qd = to_device(q, w.dtype, "cuda")
+    dec = pa.decode(qd, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens, w.num_kv_heads, w.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, dec.float().cpu().numpy().astype(np.float64))
+
+
+def test_empty_chunks_and_error_rows_without_fault():
+    w = custom(seed=12, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+               lens=[40, 77, 5, 300])
+    pool, _, tables, _, _ = replay(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    # request 1 has no new tokens
+    m = np.array([3, 0, 2, 5])
+    q, qs, got = run(w, dev, m)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
+    assert np.abs(got - ref).max() <= 2e-2
+    # request 2 claims 9 new tokens but holds 5: NaN rows for it only
+    m = np.array([3, 1, 9, 5])
+    q, qs, got = run(w, dev, m)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=[0, 1, 3])
+    bad = slice(qs[2], qs[3])
+    assert np.isnan(got[bad]).all()
+    keep = np.r_[qs[0]:qs[2], qs[3]:qs[4]]
+    assert np.abs(got[keep] - ref[keep]).max() <= 2e-2
+    # the launch sized for 4 new tokens: request 3 (5 tokens) is all NaN, the others are right
+    m = np.array([3, 1, 2, 5])
+    q, qs, got = run(w, dev, m, max_q=4)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=[0, 1, 2])
+    assert np.isnan(got[qs[3]:qs[4]]).all()
+    assert np.abs(got[: qs[3]] - ref[: qs[3]]).max() <= 2e-2
+    # a bad table entry among request 3's keys: its rows NaN, the others right
+    tb = dev.block_tables.clone()
+    tb[3, 4] = w.num_blocks + 3
+    q, qs, got = run(w, dev, m, tables=tb)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=[0, 1, 2])
+    assert np.isnan(got[qs[3]:qs[4]]).all()
+    assert np.abs(got[: qs[3]] - ref[: qs[3]]).max() <= 2e-2
