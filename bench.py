@@ -161,6 +161,132 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_passes: int = 10000):
     return res, out
 
 
+def _cpu_prefill_one(b):
+    import oracle.attention as oa
+
+    c = _CPU
+    out = oa.paged_prefill(c["q"], c["k"], c["v"], c["tables"], c["lens"], c["qs"], c["scale"], rows=[b])
+    return b, out[c["qs"][b]:c["qs"][b + 1]]
+
+
+def cpu_prefill_baseline(w, q, qs, min_seconds: float = 10.0, max_passes: int = 1000):
+    """The oracle's causal multi-token query, one request per task, until
+    ``min_seconds`` have gone by (whole requests; longest first)."""
+    import multiprocessing as mp
+
+    from oracle.cache import replay
+
+    pool, _, tables, _, _ = replay(w)
+    _CPU.update(k=pool.k, v=pool.v, tables=tables, lens=w.seq_lens, q=q, qs=qs, scale=w.scale)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("fork")
+    order = sorted(range(w.batch), key=lambda b: -int(w.seq_lens[b]))
+    out = np.zeros((int(qs[-1]), w.num_q_heads, w.head_dim))
+    done_tok, done_req = 0, 0
+    with ctx.Pool(cores, initializer=_cpu_init) as p:
+        t0 = time.perf_counter()
+        for _ in range(max_passes):
+            for b, o in p.imap_unordered(_cpu_prefill_one, order):
+                out[qs[b]:qs[b + 1]] = o
+                done_tok += int(qs[b + 1] - qs[b])
+                done_req += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                break
+    _CPU.clear()
+    return {"value": done_tok / el, "unit": "query tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done_req} requests ({done_tok} query tokens), {el:.1f} s; float64 numpy, one request per "
+                      f"task in a {cores}-process pool"}, out
+
+
+def prefill_flops(w, qs) -> float:
+    """4 * D flops per (query token, visible key, query head): QK^T and PV."""
+    tot = 0
+    for b in range(w.batch):
+        L, M = int(w.seq_lens[b]), int(qs[b + 1] - qs[b])
+        tot += M * (L - M) + M * (M + 1) // 2  # sum over i of (L - M + i + 1)
+    return 4.0 * w.head_dim * w.num_q_heads * tot
+
+
+def prefill_main(args, w):
+    """--prefill M: the last M tokens of every request are new and attend causally (pa_prefill)."""
+    import torch
+
+    import paged_kv_cache_348_amd as pa
+    from paged_kv_cache_348_amd.workload import build_device_batch, to_device
+    from synthetic import multi_query
+
+    m = np.minimum(w.seq_lens.astype(np.int64), args.prefill)
+    q, qs = multi_query(w, m, seed=args.seed)
+    T = int(qs[-1])
+    flops = prefill_flops(w, qs)
+    kv_bytes = w.kv_read_bytes()
+    log(f"multi-token query: {w.batch} requests, {args.prefill} new tokens each (T {T}), {flops / 1e9:.1f} GFLOP")
+    cpu, ref = (None, None)
+    if not args.no_cpu:
+        cpu, ref = cpu_prefill_baseline(w, q, qs, min_seconds=args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.1f} query tok/s on {cpu['cores']} cores")
+    dev = build_device_batch(w, device="cuda", partition_size=0)
+    dev.cache_append()
+    w.drop_kv()
+    qd = to_device(q, w.dtype, "cuda")
+    qsd = torch.from_numpy(qs).to("cuda")
+    out = torch.empty_like(qd)
+    maxq = int(m.max())
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pa.prefill(qd, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens, qsd, w.num_kv_heads, w.scale, maxq,
+                   out=out)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        runs.append(a.elapsed_time(b) / args.steps)
+    ms = float(np.median(runs))
+    err = None
+    if ref is not None:
+        err = float(np.abs(out.float().cpu().numpy().astype(np.float64) - ref).max())
+        log(f"full-size parity vs oracle: max abs err {err:.3e}")
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbps = kv_bytes / (ms * 1e-3) / 1e9
+    peak_tf = 2500.0 if w.dtype == "bf16" else 157.3
+    frac_m, frac_h = tflops / peak_tf, gbps / HBM_PEAK_GBPS
+    mfma_bound = frac_m >= frac_h
+    res = {
+        "metric": "causal multi-token query tokens/s over the paged cache on 1 MI355X",
+        "value": T / (ms * 1e-3),
+        "unit": "query tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v rounded to bf16; seeded lengths and block placement)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload] + f"; the last {args.prefill} tokens of each request "
+                   "are new queries with a causal mask", "name": w.name, "seed": args.seed, "batch": w.batch,
+                   "query_tokens": T, "new_tokens_per_request": args.prefill, "sum_seq_len": int(w.seq_lens.sum()),
+                   "step": "pa_prefill"},
+        "roofline": {
+            "bound": "mfma" if mfma_bound else "hbm", "kernel": "pa_prefill",
+            "achieved": tflops if mfma_bound else gbps, "peak": peak_tf if mfma_bound else HBM_PEAK_GBPS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s", "frac": frac_m if mfma_bound else frac_h,
+            "traffic": None, "flop_per_launch": flops, "algorithmic_bytes_per_launch": kv_bytes,
+            "other": {"tflops": tflops, "kv_read_gbps": gbps},
+        },
+        "runs_ms": runs,
+        "cpu_baseline": cpu,
+        "max_abs_err_vs_oracle": err,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------------- GPU
 
 
@@ -325,6 +451,9 @@ def main(argv=None):
                     help="identity: the free pool starts in address order, so each sequence's blocks are "
                          "mostly adjacent (the block-table lookup-overhead comparison)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="measure pa_prefill instead: the last N tokens of each request are new queries "
+                         "(causal multi-token query: speculative verification, chunked prefill)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -338,6 +467,8 @@ def main(argv=None):
     w = make_workload(args.workload, seed=args.seed)
     if args.block_order == "identity":
         w.free_order = np.arange(w.num_blocks, dtype=np.int32)
+    if args.prefill > 0:
+        return prefill_main(args, w)
     ps = args.partition_size
     mode = args.decode or DEFAULT_DECODE.get(args.workload, "split")
     if ps is None:
