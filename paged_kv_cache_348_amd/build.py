@@ -22,8 +22,12 @@ LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed-FP32 instructions are kept out of the device code on purpose.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-FP32 instructions are kept out of the device code on purpose.  The
+# matrix-core instructions take their accumulators in ordinary VGPRs: with
+# the compiler's default choice (accumulation registers) the decode's
+# per-step rescale of the accumulators copied all of them out and back in
+# around every PV product.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]
 
 
