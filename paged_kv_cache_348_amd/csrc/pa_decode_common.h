@@ -177,6 +177,29 @@ __device__ __forceinline__ float pair32_sum(float x) {
 __device__ __forceinline__ float wave_max16(float x) { return pair32_max(pair16_max(x)); }
 __device__ __forceinline__ float wave_sum16(float x) { return pair32_sum(pair16_sum(x)); }
 
+// Online-softmax reference update with lazy rescaling.  The running
+// reference m (per head column) only moves when a step's maximum exceeds it
+// by more than kLazyRescale (base 2): then l and the accumulators are scaled
+// by 2^(m_old - m_new) and m takes the new maximum.  Otherwise the step's
+// probabilities 2^(s - m) stay below 2^kLazyRescale (256: exact range in
+// bfloat16 and float32) and no rescale is spent.  Any reference gives the
+// same final acc / l; partial results carry their reference as m.  The
+// branch is taken by the whole wave (a ballot), always on a run's first step
+// (m = -inf).
+constexpr float kLazyRescale = 8.0f;
+
+template <int NV>
+__device__ __forceinline__ void rescale(float& m_run, float& l_run, f32x4 (&acc)[NV], float mx) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) acc[c] *= alpha;
+        m_run = m_new;
+    }
+}
+
 // One loop step: scores of the step's tokens for the G query heads, the
 // online-softmax update and the PV accumulation.  Tokens at or past L are
 // masked: their scores become -inf and their values are zeroed, since a
@@ -235,27 +258,23 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
         mx = wave_max16(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        rescale<C::NV>(m_run, l_run, acc, mx);
         float pe[8];
         float rs = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            pe[e] = __builtin_amdgcn_exp2f(s[e] - m_new);
+            pe[e] = __builtin_amdgcn_exp2f(s[e] - m_run);
             rs += pe[e];
         }
         rs = wave_sum16(rs);
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
+        l_run += rs;
         const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]), pack_bf16x2(pe[4], pe[5]),
                           pack_bf16x2(pe[6], pe[7])};
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-        for (int c = 0; c < C::NV; ++c) {
-            acc[c] *= alpha;
+        for (int c = 0; c < C::NV; ++c)
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.v[c]), pb, acc[c],
                                                             0, 0, 0);
-        }
     } else {
         // ---- scores: one 16-token tile, row 4j+i <-> token 4j+i
         f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
@@ -280,21 +299,18 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
         }
         float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         mx = wave_max16(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        rescale<C::NV>(m_run, l_run, acc, mx);
         float pe[4];
         float rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pe[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
+            pe[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
             rs += pe[i];
         }
         rs = wave_sum16(rs);
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
+        l_run += rs;
 #pragma unroll
         for (int c = 0; c < C::NV; ++c) {
-            acc[c] *= alpha;
             const f32x4 vf = __builtin_bit_cast(f32x4, cur.v[c]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
