@@ -234,10 +234,13 @@ def prefill_main(args, w):
     out = torch.empty_like(qd)
     maxq = int(m.max())
     stream = torch.cuda.current_stream()
+    wsb = pa.prefill_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, maxq)
+    ws = pa.new_workspace(wsb) if wsb else None  # verification sizes: the balanced split's workspace, made once
+    log(f"pa_prefill path: {'balanced split' if wsb else 'query tiles'}")
 
     def call():
         pa.prefill(qd, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens, qsd, w.num_kv_heads, w.scale, maxq,
-                   out=out)
+                   out=out, workspace=ws)
 
     for _ in range(args.warmup):
         call()
@@ -271,7 +274,7 @@ def prefill_main(args, w):
         "config": {"workload": WORKLOAD_TEXT[args.workload] + f"; the last {args.prefill} tokens of each request "
                    "are new queries with a causal mask", "name": w.name, "seed": args.seed, "batch": w.batch,
                    "query_tokens": T, "new_tokens_per_request": args.prefill, "sum_seq_len": int(w.seq_lens.sum()),
-                   "step": "pa_prefill"},
+                   "step": "pa_prefill (" + ("balanced split" if wsb else "query tiles") + ")"},
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm", "kernel": "pa_prefill",
             "achieved": tflops if mfma_bound else gbps, "peak": peak_tf if mfma_bound else HBM_PEAK_GBPS,

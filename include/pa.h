@@ -184,6 +184,16 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  *                0 allowed)
  *   out          device, [num_query_tokens][num_q_heads][head_dim], dtype
  *   max_query_len  >= every M_b (sizes the launch)
+ *   workspace    may be NULL.  When pa_prefill_workspace_bytes() is not 0
+ *                (max_query_len * (num_q_heads / num_kv_heads) <= 16 and
+ *                num_seqs <= 1024: verification-sized chunks) and the caller
+ *                passes a workspace of at least that size, 256-byte aligned,
+ *                the chunks run on pa_decode's balanced split (each request's
+ *                (token, head) pairs are one wave's columns); its counter
+ *                bytes (pa_decode_counter_bytes) must be zero before the
+ *                first use and are left zero, as for pa_decode.  Otherwise a
+ *                kernel with one wave per (kv-head, tile of query tokens,
+ *                request) runs and the workspace is not used.
  *   num_q_heads / num_kv_heads <= 16; the other arguments as for pa_decode.
  * Error rows: a request with M_b > L_b, M_b > max_query_len, or L_b longer
  * than its table holds gets NaN in all its rows; a table entry outside
@@ -191,11 +201,14 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * request whose query_start pair is out of order or outside
  * [0, num_query_tokens] writes nothing.  Nothing faults.
  * ------------------------------------------------------------------------ */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_query_len);
+
 pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                      const int32_t* seq_lens, const int32_t* query_start, int32_t num_kv_heads, float scale,
                      void* out, void* stream, int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                     pa_dtype dtype, int32_t max_query_len);
+                     pa_dtype dtype, int32_t max_query_len, void* workspace, size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
  * Copy whole blocks from one pool to another with the same block shape:

@@ -31,7 +31,7 @@ __all__ = [
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
     "new_workspace", "SharedPrefixPlan", "plan_shared_prefix", "decode_shared_prefix",
     "decode_shared_prefix_workspace_bytes", "shared_prefix_max_group", "simulate_memory", "PA_MEM_CONTIGUOUS",
-    "PA_MEM_PAGED", "swap_blocks", "prefill",
+    "PA_MEM_PAGED", "swap_blocks", "prefill", "prefill_workspace_bytes",
 ]
 
 
@@ -314,11 +314,21 @@ def simulate_memory(arrival, prompt, reply, capacity_slots: int, scheme: int, pa
     return {name: int(getattr(st, name)) for name, _ in MemStats._fields_}
 
 
+def prefill_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            max_query_len: int) -> int:
+    """Workspace for the balanced path of pa_prefill (0: that path does not apply)."""
+    return int(lib().pa_prefill_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_query_len))
+
+
 def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_heads: int, scale: float,
-            max_query_len: int, out=None, stream=None):
+            max_query_len: int, out=None, stream=None, workspace=None, balanced: bool = True):
     """Causal multi-token query over the paged cache (pa_prefill): q [T, Hq, D]
     holds each request's new tokens, rows query_start[b] .. query_start[b+1]-1;
-    the last M_b of its seq_lens[b] cached tokens are those tokens.  Returns out [T, Hq, D]."""
+    the last M_b of its seq_lens[b] cached tokens are those tokens.  Returns out [T, Hq, D].
+
+    Verification-sized chunks (max_query_len * G <= 16) run on the balanced
+    split when ``balanced`` (a zero-filled workspace is made when none is
+    given); otherwise, or with ``balanced=False``, the per-tile kernel runs."""
     torch = _torch()
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     if hkv != num_kv_heads:
@@ -337,11 +347,17 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_hea
         raise ValueError("out must match q")
     if B == 0 or T == 0:
         return out
+    ws_ptr, ws_bytes = None, 0
+    need = prefill_workspace_bytes(B, hq, hkv, d, int(max_query_len)) if balanced else 0
+    if need:
+        if workspace is None:
+            workspace = new_workspace(need, q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     check(lib().pa_prefill(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
                            _dev(query_start, "query_start"), hkv, float(scale), _dev(out, "out"), _stream_ptr(stream),
-                           B, T, hq, d, bs, nb, block_tables.shape[1], _dtype_code(q.dtype), int(max_query_len)),
-          "pa_prefill")
+                           B, T, hq, d, bs, nb, block_tables.shape[1], _dtype_code(q.dtype), int(max_query_len),
+                           ws_ptr, ws_bytes), "pa_prefill")
     return out
 
 

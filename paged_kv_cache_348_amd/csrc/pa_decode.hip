@@ -217,11 +217,15 @@ struct StepCursor {
     int ls;   // step within the (sequence, kv-head) segment
     int nst;  // steps of that segment
     int L;    // length of sequence b
+    int t0;   // multi-token query: first query row of sequence b
+    int M;    // multi-token query: its query tokens (the last M of its L)
 };
 
 // Advance one step, skipping sequences without steps.  Called only while
 // a next step exists, so a later sequence with steps exists too.
-__device__ __forceinline__ void cursor_next(StepCursor& c, const int32_t* s_steps, const int32_t* s_len, int Hkv) {
+template <bool MULTI>
+__device__ __forceinline__ void cursor_next(StepCursor& c, const int32_t* s_steps, const int32_t* s_len,
+                                            const int32_t* s_qs, int Hkv) {
     if (++c.ls < c.nst) return;
     c.ls = 0;
     if (++c.g < Hkv) return;
@@ -231,6 +235,20 @@ __device__ __forceinline__ void cursor_next(StepCursor& c, const int32_t* s_step
     } while (uniform(s_steps[c.b]) == 0);
     c.nst = uniform(s_steps[c.b]);
     c.L = uniform(s_len[c.b]);
+    if constexpr (MULTI) {
+        c.t0 = uniform(s_qs[c.b]);
+        c.M = uniform(s_qs[c.b + 1]) - c.t0;
+    }
+}
+
+// Output row of column n of segment (b, g): head g*G + n for a decode; for a
+// multi-token query, columns are (token, head) pairs, token-major.
+template <bool MULTI>
+__device__ __forceinline__ int64_t col_row(int b, int g, int t0, int n, int Hq, int G) {
+    if constexpr (MULTI)
+        return (int64_t)(t0 + n / G) * Hq + g * G + n % G;
+    else
+        return (int64_t)b * Hq + g * G + n;
 }
 
 // What the load stage of a step needs: its sequence length and the
@@ -270,11 +288,16 @@ __device__ __forceinline__ void fetch_step(StepInfo& f, const StepCursor& c, con
 // head G-1.  Their scores, softmax statistics and outputs stay in their own
 // columns and are never stored, and the loaded registers are used as they
 // arrive (touching them here would make this stage wait for the load).
-template <bool BF16, int D, int BS>
+template <bool BF16, int D, int BS, bool MULTI>
 __device__ __forceinline__ void load_q_all(typename DecodeCfg<BF16, D, BS>::QRegs& qr, const void* __restrict__ q_,
-                                           int64_t row0, int n, int j, int G) {
+                                           const StepCursor& c, int Hq, int n, int j, int G, int qi, int qh) {
     using C = DecodeCfg<BF16, D, BS>;
-    const char* qp = reinterpret_cast<const char*>(q_) + (row0 + min(n, G - 1)) * D * C::ES;
+    int64_t row;
+    if constexpr (MULTI)  // column (qi, qh) = (n / G, n % G); past the last token: the last column
+        row = (int64_t)(c.t0 + min(qi, c.M - 1)) * Hq + c.g * G + (qi < c.M ? qh : G - 1);
+    else
+        row = (int64_t)c.b * Hq + c.g * G + min(n, G - 1);
+    const char* qp = reinterpret_cast<const char*>(q_) + row * D * C::ES;
 #pragma unroll
     for (int c = 0; c < C::NKC; ++c) qr[c] = ld16(qp + (int64_t)(4 * c + j) * 16);
 }
@@ -284,17 +307,20 @@ struct CutPiece {
     bool valid;
     int b, g;
     int64_t seg0, seg1;  // the segment's global steps [seg0, seg1)
+    int t0, M;           // multi-token query: the segment's rows
 };
 
 // Count a piece in; the wave that brings the segment's counter to its
 // piece count merges every piece (log-sum-exp rule), writes the G rows and
 // puts the counter back to zero.
-template <bool BF16, int D, int BS>
+template <bool BF16, int D, int BS, bool MULTI>
 __device__ __forceinline__ void count_in(const CutPiece& cp, const float* __restrict__ slot_o,
                                          const float* __restrict__ slot_ml, int32_t* __restrict__ counters,
                                          void* __restrict__ out_, int64_t S, int nw, int Hq, int Hkv, int G, int lane,
                                          int n, int j) {
     using C = DecodeCfg<BF16, D, BS>;
+    const int SC = MULTI ? 16 : G;              // columns per partial slot
+    const int ncol = MULTI ? cp.M * G : G;      // columns with an output row
     const int w0 = wave_of_step(cp.seg0, S, nw);
     const int w1 = wave_of_step(cp.seg1 - 1, S, nw);
     int32_t* cnt = counters + (int64_t)cp.b * Hkv + cp.g;
@@ -302,11 +328,11 @@ __device__ __forceinline__ void count_in(const CutPiece& cp, const float* __rest
     if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0, 64);
     if (old != w1 - w0) return;
-    if (n < G) {
+    if (n < ncol) {
         float M = -INFINITY;
         for (int k = w0; k <= w1; ++k) {
             const int64_t sk = 2 * (int64_t)k + ((k == w0 && cp.seg0 != S * k / nw) ? 1 : 0);
-            M = fmaxf(M, coherent_load(reinterpret_cast<const uint64_t*>(slot_ml + (sk * G + n) * 2)).x);
+            M = fmaxf(M, coherent_load(reinterpret_cast<const uint64_t*>(slot_ml + (sk * SC + n) * 2)).x);
         }
         RunState<BF16, D, BS> Mg;
         Mg.m = M;
@@ -316,10 +342,10 @@ __device__ __forceinline__ void count_in(const CutPiece& cp, const float* __rest
         for (int c = 0; c < C::NV; ++c) Mg.acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int k = w0; k <= w1; ++k) {
             const int64_t sk = 2 * (int64_t)k + ((k == w0 && cp.seg0 != S * k / nw) ? 1 : 0);
-            const float2 ml = coherent_load(reinterpret_cast<const uint64_t*>(slot_ml + (sk * G + n) * 2));
+            const float2 ml = coherent_load(reinterpret_cast<const uint64_t*>(slot_ml + (sk * SC + n) * 2));
             const float wt = __builtin_amdgcn_exp2f(ml.x - M);
             Mg.l += wt * ml.y;
-            const uint64_t* po = reinterpret_cast<const uint64_t*>(slot_o + (sk * G + n) * D);
+            const uint64_t* po = reinterpret_cast<const uint64_t*>(slot_o + (sk * SC + n) * D);
 #pragma unroll
             for (int c = 0; c < C::NV; ++c) {
                 const int e = (16 * c + 4 * j) / 2;
@@ -327,7 +353,7 @@ __device__ __forceinline__ void count_in(const CutPiece& cp, const float* __rest
                 Mg.acc[c] += wt * f32x4{lo.x, lo.y, hi.x, hi.y};
             }
         }
-        store_out<BF16, D, BS>(out_, (int64_t)cp.b * Hq + cp.g * G, Mg, n, j, G);
+        store_out<BF16, D, BS>(out_, col_row<MULTI>(cp.b, cp.g, cp.t0, n, Hq, G) - n, Mg, n, j, ncol);
     }
     if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -335,20 +361,22 @@ __device__ __forceinline__ void count_in(const CutPiece& cp, const float* __rest
 // Finish the piece whose last step was just computed: a whole segment is
 // written out; a cut one leaves its partial in slot (w, 0) if it is the
 // wave's first piece, else (w, 1), and is remembered for counting in.
-template <bool BF16, int D, int BS>
+template <bool BF16, int D, int BS, bool MULTI>
 __device__ __forceinline__ void finish_piece(const RunState<BF16, D, BS>& St, const StepCursor& cc, bool seg_begin,
                                              bool& first_piece, CutPiece& cut0, CutPiece& cut1,
                                              const int64_t* s_first, float* __restrict__ slot_o,
                                              float* __restrict__ slot_ml, void* __restrict__ out_, int w, int Hq,
                                              int G, int n, int j) {
     using C = DecodeCfg<BF16, D, BS>;
+    const int SC = MULTI ? 16 : G;          // columns per partial slot
+    const int ncol = MULTI ? cc.M * G : G;  // columns with an output row
     const bool complete = seg_begin && cc.ls == cc.nst - 1;
     if (complete) {
-        store_out<BF16, D, BS>(out_, (int64_t)cc.b * Hq + cc.g * G, St, n, j, G);
+        store_out<BF16, D, BS>(out_, col_row<MULTI>(cc.b, cc.g, cc.t0, n, Hq, G) - n, St, n, j, ncol);
     } else {
         const int64_t slot = 2 * (int64_t)w + (first_piece ? 0 : 1);
-        if (n < G) {
-            uint64_t* po = reinterpret_cast<uint64_t*>(slot_o + (slot * G + n) * D);
+        if (n < ncol) {
+            uint64_t* po = reinterpret_cast<uint64_t*>(slot_o + (slot * SC + n) * D);
 #pragma unroll
             for (int c = 0; c < C::NV; ++c) {
                 const f32x4 a = St.bad ? f32x4{NAN, NAN, NAN, NAN} : St.acc[c];
@@ -357,11 +385,11 @@ __device__ __forceinline__ void finish_piece(const RunState<BF16, D, BS>& St, co
                 coherent_store(po + e + 1, a[2], a[3]);
             }
             if (j == 0)
-                coherent_store(reinterpret_cast<uint64_t*>(slot_ml + (slot * G + n) * 2), St.bad ? 0.0f : St.m,
+                coherent_store(reinterpret_cast<uint64_t*>(slot_ml + (slot * SC + n) * 2), St.bad ? 0.0f : St.m,
                                St.bad ? 1.0f : St.l);
         }
         const int64_t seg0 = uniform64(s_first[cc.b]) + (int64_t)cc.g * cc.nst;
-        const CutPiece cp = {true, cc.b, cc.g, seg0, seg0 + cc.nst};
+        const CutPiece cp = {true, cc.b, cc.g, seg0, seg0 + cc.nst, cc.t0, cc.M};
         if (first_piece)
             cut0 = cp;
         else
@@ -375,9 +403,11 @@ __device__ __forceinline__ void finish_piece(const RunState<BF16, D, BS>& St, co
 // x+1 with the table entries fetched one iteration earlier, (2) fetches the
 // entries of step x+2 with scalar loads and (3) computes step x.  A piece
 // ends where its segment ends or at the wave's last step.
-template <bool BF16, int D, int BS>
+template <bool BF16, int D, int BS, bool MULTI>
 struct BalancedWave {
     using C = DecodeCfg<BF16, D, BS>;
+    const int32_t* s_qs;  // multi-token query: query_start in LDS
+    int qi, qh;           // multi-token query: this lane's column as (token n / G, head n % G)
     const void* q_;
     const char* kc;
     const char* vc;
@@ -404,7 +434,7 @@ struct BalancedWave {
                                           const StepInfo& f) {
         const int64_t hb = (int64_t)c.g * C::TILE * C::ES;
         issue_step_e<BF16, D, BS>(buf, kc + hb, vc + hb, blk_bytes, f.e, c.ls * C::STEP, c.L, n, j);
-        load_q_all<BF16, D, BS>(q, q_, (int64_t)c.b * Hq + c.g * G, n, j, G);
+        load_q_all<BF16, D, BS, MULTI>(q, q_, c, Hq, n, j, G, qi, qh);
     }
 
     // step x0 loaded into (buf, q); entries of x0+1 fetched
@@ -415,18 +445,25 @@ struct BalancedWave {
         issue(buf, q, cc, f0);
         ci = cc;
         if (x0 + 1 < wend) {
-            cursor_next(ci, s_steps, s_len, Hkv);
+            cursor_next<MULTI>(ci, s_steps, s_len, s_qs, Hkv);
             fetch_step<BF16, D, BS>(fe, ci, tables, max_blocks, num_blocks);
         }
     }
 
     __device__ __forceinline__ void compute(StepRegs<BF16, D, BS>& buf, const typename C::QRegs& q) {
-        compute_step<BF16, D, BS>(buf, q, St.m, St.l, St.acc, cc.ls * C::STEP, cc.L, j, scale_log2);
+        if constexpr (MULTI) {
+            // column n is query token n / G at position L - M + n / G: it sees keys up to there
+            const int lim = cc.L - cc.M + 1;
+            compute_step<BF16, D, BS, true>(buf, q, St.m, St.l, St.acc, cc.ls * C::STEP, cc.L, j, scale_log2,
+                                            lim + min(qi, cc.M - 1), lim);
+        } else {
+            compute_step<BF16, D, BS>(buf, q, St.m, St.l, St.acc, cc.ls * C::STEP, cc.L, j, scale_log2);
+        }
         St.bad |= bad_c;
     }
 
     __device__ __forceinline__ void finish() {
-        finish_piece<BF16, D, BS>(St, cc, seg_begin, first_piece, cut0, cut1, s_first, slot_o, slot_ml, out_, w, Hq,
+        finish_piece<BF16, D, BS, MULTI>(St, cc, seg_begin, first_piece, cut0, cut1, s_first, slot_o, slot_ml, out_, w, Hq,
                                   G, n, j);
     }
 
@@ -437,7 +474,7 @@ struct BalancedWave {
         bad_i = fe.bad;
         StepCursor cf = ci;
         if (x + 2 < wend) {
-            cursor_next(cf, s_steps, s_len, Hkv);
+            cursor_next<MULTI>(cf, s_steps, s_len, s_qs, Hkv);
             fetch_step<BF16, D, BS>(fe, cf, tables, max_blocks, num_blocks);
         }
         // keep the compiler from hoisting the compute (and its wait) above the loads
@@ -475,16 +512,20 @@ struct BalancedWave {
 // counts its cut pieces in, and the wave that completes a segment's count
 // merges its pieces, writes the rows and puts the counter back to zero.
 // No wave waits for another.
-template <bool BF16, int D, int BS>
+// MULTI: a multi-token query (query_start given): segment (b, g) has the
+// M_b * G columns (token, head) of sequence b's M_b new tokens, M_b * G <= 16,
+// each masked causally at its own position.
+template <bool BF16, int D, int BS, bool MULTI>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(
     const void* __restrict__ q_, const void* __restrict__ kc_, const void* __restrict__ vc_,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens, void* __restrict__ out_,
     float* __restrict__ slot_o, float* __restrict__ slot_ml, int32_t* __restrict__ counters, int B, int Hq,
-    int Hkv, int G, int max_blocks, int num_blocks, float scale_log2) {
+    int Hkv, int G, int max_blocks, int num_blocks, float scale_log2, const int32_t* __restrict__ q_start, int T) {
     using C = DecodeCfg<BF16, D, BS>;
     __shared__ int64_t s_first[kBalancedMaxSeqs];  // global step where sequence b's segments start
     __shared__ int32_t s_steps[kBalancedMaxSeqs];  // steps per segment of sequence b (0: no work)
     __shared__ int32_t s_len[kBalancedMaxSeqs];    // length of sequence b
+    __shared__ int32_t s_qs[MULTI ? kBalancedMaxSeqs + 1 : 1];  // multi-token query: query_start
     const int lane = threadIdx.x;
     const int n = lane & 15;
     const int j = lane >> 4;
@@ -505,7 +546,17 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
         if (64 * c >= B) break;
         const int b = 64 * c + lane;
         const int L = lv[c];
-        const bool ok = b < B && L > 0 && (int64_t)L <= (int64_t)max_blocks * BS;
+        bool ok = b < B && L > 0 && (int64_t)L <= (int64_t)max_blocks * BS;
+        if constexpr (MULTI) {
+            // M new tokens at the end of the L cached ones, M * G columns at most 16
+            const int t0 = b < B ? q_start[b] : 0, t1 = b < B ? q_start[b + 1] : 0;
+            const int M = t1 - t0;
+            ok = ok && t0 >= 0 && t1 <= T && M >= 1 && M <= L && M * G <= 16;
+            if (b < B) {
+                s_qs[b] = t0;
+                if (b == B - 1) s_qs[B] = t1;
+            }
+        }
         const int st = ok ? (L + C::STEP - 1) / C::STEP : 0;
         const int64_t v = (int64_t)st * Hkv;
         const int64_t incl = wave_incl_scan(v, lane);
@@ -524,7 +575,16 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     for (int b = w; b < B; b += gridDim.x) {
         if (s_steps[b] == 0) {
             const int L = lens[b];
-            fill_rows<BF16, D>(out_, (int64_t)b * Hq, Hq, L <= 0 ? 0.0f : __builtin_nanf(""), lane);
+            if constexpr (MULTI) {
+                // rows of a request that cannot be served (more new tokens than
+                // cached ones or than the columns hold, or a bad length): NaN;
+                // malformed query offsets: nothing is written
+                const int t0 = q_start[b], t1 = q_start[b + 1];
+                if (t0 >= 0 && t1 <= T && t1 > t0)
+                    fill_rows<BF16, D>(out_, (int64_t)t0 * Hq, (t1 - t0) * Hq, __builtin_nanf(""), lane);
+            } else {
+                fill_rows<BF16, D>(out_, (int64_t)b * Hq, Hq, L <= 0 ? 0.0f : __builtin_nanf(""), lane);
+            }
         }
     }
     const int nw = (int)min((int64_t)gridDim.x, S);
@@ -543,6 +603,12 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     cc.b = uniform(lo);
     cc.nst = uniform(s_steps[cc.b]);
     cc.L = uniform(s_len[cc.b]);
+    cc.t0 = 0;
+    cc.M = 1;
+    if constexpr (MULTI) {
+        cc.t0 = uniform(s_qs[cc.b]);
+        cc.M = uniform(s_qs[cc.b + 1]) - cc.t0;
+    }
     {
         const int64_t off = wbeg - uniform64(s_first[cc.b]);
         cc.g = (int)(off / cc.nst);
@@ -551,7 +617,10 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
 
     // 4. the pipeline: stage buffers A and B alternate, so no loaded
     //    register is ever copied (a copy would have to wait for its load)
-    BalancedWave<BF16, D, BS> W;
+    BalancedWave<BF16, D, BS, MULTI> W;
+    W.s_qs = s_qs;
+    W.qi = MULTI ? n / G : 0;
+    W.qh = MULTI ? n % G : 0;
     W.q_ = q_;
     W.kc = reinterpret_cast<const char*>(kc_);
     W.vc = reinterpret_cast<const char*>(vc_);
@@ -576,8 +645,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     W.cc = cc;
     W.seg_begin = cc.ls == 0;
     W.first_piece = true;
-    W.cut0 = CutPiece{false, 0, 0, 0, 0};
-    W.cut1 = CutPiece{false, 0, 0, 0, 0};
+    W.cut0 = CutPiece{false, 0, 0, 0, 0, 0, 0};
+    W.cut1 = CutPiece{false, 0, 0, 0, 0, 0, 0};
     run_init(W.St);
 
     StepRegs<BF16, D, BS> bufA, bufB;
@@ -599,8 +668,10 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     // 5. count the cut pieces in (their partials must be at the coherent level first)
     if (cut0.valid || cut1.valid) {
         __builtin_amdgcn_s_waitcnt(0);
-        if (cut0.valid) count_in<BF16, D, BS>(cut0, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
-        if (cut1.valid) count_in<BF16, D, BS>(cut1, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
+        if (cut0.valid)
+            count_in<BF16, D, BS, MULTI>(cut0, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
+        if (cut1.valid)
+            count_in<BF16, D, BS, MULTI>(cut1, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
     }
 }
 
@@ -659,6 +730,8 @@ struct Launch {
     int32_t* counters;
     int B, Hq, Hkv, max_blocks, num_blocks, PS, P_max;
     bool balanced;
+    const int32_t* q_start;  // set: a multi-token query on the balanced split (T query rows)
+    int T;
     float sl2;
     hipStream_t stream;
 };
@@ -667,9 +740,14 @@ template <bool BF16, int D, int BS>
 hipError_t launch_decode(const Launch& a) {
     const int G = a.Hq / a.Hkv;
     if (a.balanced) {
-        hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS>), dim3((unsigned)balanced_waves()), dim3(64), 0,
-                           a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml, a.counters, a.B, a.Hq,
-                           a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2);
+        if (a.q_start)
+            hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, true>), dim3((unsigned)balanced_waves()),
+                               dim3(64), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
+                               a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, a.q_start, a.T);
+        else
+            hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, false>), dim3((unsigned)balanced_waves()),
+                               dim3(64), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
+                               a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, nullptr, 0);
         return hipGetLastError();
     }
     dim3 grid((unsigned)a.Hkv, (unsigned)a.P_max, (unsigned)a.B);
@@ -780,6 +858,62 @@ extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v
         e = head_dim == 128 ? dispatch_bs<false, 128>(block_size, a) : dispatch_bs<false, 64>(block_size, a);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
+
+// ---- multi-token query on the balanced split (pa_prefill's path for
+// requests whose new tokens fit one wave's 16 columns: M * G <= 16)
+namespace pa_internal {
+
+size_t multi_balanced_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_query_len) {
+    if (num_seqs <= 0 || num_seqs > pa::kBalancedMaxSeqs || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+        head_dim <= 0 || max_query_len <= 0 || (int64_t)max_query_len * (num_q_heads / num_kv_heads) > 16)
+        return 0;
+    const size_t slots = 2 * (size_t)pa::kBalancedMaxWaves * 16;
+    return counter_bytes(num_seqs, num_kv_heads) + align_up(slots * head_dim * sizeof(float)) +
+           align_up(slots * 2 * sizeof(float));
+}
+
+// Arguments are validated by the caller (pa_prefill); the workspace holds at
+// least multi_balanced_workspace_bytes().
+pa_status multi_balanced_launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                const int32_t* seq_lens, const int32_t* query_start, int32_t num_kv_heads, float scale,
+                                void* out, void* stream, int32_t num_seqs, int32_t num_query_tokens,
+                                int32_t num_q_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, pa_dtype dtype, void* workspace) {
+    Launch a{};
+    char* ws = reinterpret_cast<char*>(workspace);
+    const size_t cnt = counter_bytes(num_seqs, num_kv_heads);
+    const size_t slots = 2 * (size_t)pa::kBalancedMaxWaves * 16;
+    a.counters = reinterpret_cast<int32_t*>(ws);
+    a.po = reinterpret_cast<float*>(ws + cnt);
+    a.pml = reinterpret_cast<float*>(ws + cnt + align_up(slots * head_dim * sizeof(float)));
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.tables = block_tables;
+    a.lens = seq_lens;
+    a.out = out;
+    a.B = num_seqs;
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.PS = 0;
+    a.P_max = 1;
+    a.balanced = true;
+    a.q_start = query_start;
+    a.T = num_query_tokens;
+    a.sl2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == PA_BF16)
+        e = head_dim == 128 ? dispatch_bs<true, 128>(block_size, a) : dispatch_bs<true, 64>(block_size, a);
+    else
+        e = head_dim == 128 ? dispatch_bs<false, 128>(block_size, a) : dispatch_bs<false, 64>(block_size, a);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace pa_internal
 
 extern "C" size_t pa_decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads) {
     if (num_seqs <= 0 || num_kv_heads <= 0) return 0;

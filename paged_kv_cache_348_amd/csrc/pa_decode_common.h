@@ -184,15 +184,16 @@ __device__ __forceinline__ float wave_sum16(float x) { return pair32_sum(pair16_
 // probabilities 2^(s - m) stay below 2^kLazyRescale (256: exact range in
 // bfloat16 and float32) and no rescale is spent.  Any reference gives the
 // same final acc / l; partial results carry their reference as m.  The
-// branch is taken by the whole wave (a ballot), always on a run's first step
-// (m = -inf).
+// branch is taken by the whole wave (a ballot), on a run's first step with a
+// visible key (m = -inf before it).
 constexpr float kLazyRescale = 8.0f;
 
 template <int NV>
 __device__ __forceinline__ void rescale(float& m_run, float& l_run, f32x4 (&acc)[NV], float mx) {
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale)) {
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // a column with no visible key yet (causal runs) keeps m = -inf and l = acc = 0
+        const float alpha = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int c = 0; c < NV; ++c) acc[c] *= alpha;
@@ -259,11 +260,14 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
         mx = wave_max16(mx);
         rescale<C::NV>(m_run, l_run, acc, mx);
+        // causal: a run cut mid-sequence can start with steps whose keys are all
+        // past a column's position; that column keeps m = -inf and gets p = 0
+        const float mref = (CAUSAL && m_run == -INFINITY) ? 0.0f : m_run;
         float pe[8];
         float rs = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            pe[e] = __builtin_amdgcn_exp2f(s[e] - m_run);
+            pe[e] = __builtin_amdgcn_exp2f(s[e] - mref);
             rs += pe[e];
         }
         rs = wave_sum16(rs);
@@ -300,11 +304,12 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
         float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         mx = wave_max16(mx);
         rescale<C::NV>(m_run, l_run, acc, mx);
+        const float mref = (CAUSAL && m_run == -INFINITY) ? 0.0f : m_run;  // as in the bf16 path
         float pe[4];
         float rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pe[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
+            pe[i] = __builtin_amdgcn_exp2f(s[i] - mref);
             rs += pe[i];
         }
         rs = wave_sum16(rs);

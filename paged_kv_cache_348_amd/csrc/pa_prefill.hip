@@ -144,6 +144,18 @@ __global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_
 
 // ---------------------------------------------------------------------------- host side
 
+// The balanced split of the decode (pa_decode.hip) serves multi-token
+// queries whose M * G columns fit one wave (up to 16).
+namespace pa_internal {
+size_t multi_balanced_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_query_len);
+pa_status multi_balanced_launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                const int32_t* seq_lens, const int32_t* query_start, int32_t num_kv_heads, float scale,
+                                void* out, void* stream, int32_t num_seqs, int32_t num_query_tokens,
+                                int32_t num_q_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, pa_dtype dtype, void* workspace);
+}  // namespace pa_internal
+
 namespace {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -187,11 +199,17 @@ hipError_t prefill_bs(int BS, int cols, const PrefillLaunch& a) {
 
 }  // namespace
 
+extern "C" size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t max_query_len) {
+    return pa_internal::multi_balanced_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_query_len);
+}
+
 extern "C" pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                 const int32_t* seq_lens, const int32_t* query_start, int32_t num_kv_heads, float scale,
                                 void* out, void* stream, int32_t num_seqs, int32_t num_query_tokens,
                                 int32_t num_q_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                int32_t max_blocks_per_seq, pa_dtype dtype, int32_t max_query_len) {
+                                int32_t max_blocks_per_seq, pa_dtype dtype, int32_t max_query_len, void* workspace,
+                                size_t workspace_bytes) {
     if (num_seqs < 0 || num_query_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 ||
         max_blocks_per_seq < 0 || max_query_len < 0 || !std::isfinite(scale))
         return PA_ERR_INVALID_ARG;
@@ -210,6 +228,17 @@ extern "C" pa_status pa_prefill(const void* q, const void* k_cache, const void* 
         (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
         (reinterpret_cast<uintptr_t>(query_start) & 3u))
         return PA_ERR_INVALID_ARG;
+    // verification-sized chunks: the balanced split (every request's tokens
+    // fit one wave's columns) when the caller brings its workspace
+    const size_t wneed = pa_internal::multi_balanced_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                                     max_query_len);
+    if (wneed && workspace) {
+        if (workspace_bytes < wneed || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return PA_ERR_INVALID_ARG;
+        return pa_internal::multi_balanced_launch(q, k_cache, v_cache, block_tables, seq_lens, query_start,
+                                                  num_kv_heads, scale, out, stream, num_seqs, num_query_tokens,
+                                                  num_q_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                                  dtype, workspace);
+    }
     PrefillLaunch a{};
     a.q = q;
     a.kc = k_cache;

@@ -415,7 +415,8 @@ def prefill_call(**kw):
              stream=None, B=4, T=16, hq=32, d=128, bs=16, nb=100, mb=8, dt=1, mq=4)
     a.update(kw)
     return _l().pa_prefill(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["qs"], a["hkv"], a["scale"], a["out"],
-                           a["stream"], a["B"], a["T"], a["hq"], a["d"], a["bs"], a["nb"], a["mb"], a["dt"], a["mq"])
+                           a["stream"], a["B"], a["T"], a["hq"], a["d"], a["bs"], a["nb"], a["mb"], a["dt"], a["mq"],
+                           a.get("ws"), a.get("wsb", 0))
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -434,6 +435,17 @@ def prefill_call(**kw):
     (dict(B=0, q=None, kc=None, vc=None, bt=None, sl=None, qs=None, out=None), pa.PA_OK),
     (dict(T=0, q=None, out=None), pa.PA_OK),
     (dict(mq=0), pa.PA_OK),
+    (dict(ws=fake(0x10100), wsb=16), pa.PA_ERR_INVALID_ARG),   # balanced path: workspace too small
+    (dict(ws=fake(0x10010), wsb=1 << 30), pa.PA_ERR_INVALID_ARG),  # not 256-byte aligned
 ])
 def test_prefill_rejects_bad_arguments(kw, expect):
     assert prefill_call(**kw) == expect
+
+
+def test_prefill_workspace_size():
+    # 4 new tokens x 4 heads = 16 columns: the balanced path, with counters and 16-column slots
+    n = pa.prefill_workspace_bytes(64, 32, 8, 128, 4)
+    assert n >= _l().pa_decode_counter_bytes(64, 8) + 2 * 2048 * 16 * 130 * 4 and n % 256 == 0
+    assert pa.prefill_workspace_bytes(64, 32, 8, 128, 5) == 0   # 20 columns: the tile kernel
+    assert pa.prefill_workspace_bytes(1025, 32, 8, 128, 4) == 0
+    assert pa.prefill_workspace_bytes(8, 8, 8, 64, 16) > 0      # G = 1: 16 tokens

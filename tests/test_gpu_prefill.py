@@ -31,14 +31,14 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run(w, dev, m, seed=1, max_q=None, tables=None, lens=None, qs_override=None):
+def run(w, dev, m, seed=1, max_q=None, tables=None, lens=None, qs_override=None, balanced=True):
     q, qs = multi_query(w, m, seed=seed)
     if qs_override is not None:
         qs = qs_override
     qd = to_device(q, w.dtype, "cuda")
     out = pa.prefill(qd, dev.k_cache, dev.v_cache, dev.block_tables if tables is None else tables,
                      dev.seq_lens if lens is None else lens, torch.from_numpy(qs).to("cuda"), w.num_kv_heads,
-                     w.scale, int(max(m)) if max_q is None else max_q)
+                     w.scale, int(max(m)) if max_q is None else max_q, balanced=balanced)
     torch.cuda.synchronize()
     return q, qs, out.float().cpu().numpy().astype(np.float64)
 
@@ -55,6 +55,15 @@ CASES = [
     ("full-f32-G1-D64", "f32", 8, 8, 64, 16, [14, 60, 1, 33], "L"),
     ("chunk-f32-G4-D128-bs8", "f32", 32, 8, 128, 8, [90, 41, 160], 20),
     ("chunk-f32-G2-D128-bs32", "f32", 6, 3, 128, 32, [70, 129], 0.4),
+    # verification sizes that fit one wave's 16 columns: the balanced split
+    ("verify2-bf16-G4-long", "bf16", 32, 8, 128, 16, [3000, 17, 1, 700, 2049], 2),
+    ("verify3-bf16-G4-bs8", "bf16", 32, 8, 128, 8, [90, 400, 33, 3], 3),
+    ("verify4-bf16-G4-bs32", "bf16", 32, 8, 128, 32, [1500, 260, 4, 999], 4),
+    ("verify2-bf16-G8", "bf16", 64, 8, 128, 16, [300, 1200, 2], 2),
+    ("verify16-bf16-G1-D64", "bf16", 8, 8, 64, 16, [200, 130, 64, 16], 16),
+    ("verify1-bf16-G16", "bf16", 16, 1, 128, 16, [100, 17, 250], 1),
+    ("verify8-f32-G2-D64", "f32", 8, 4, 64, 16, [300, 77, 8], 8),
+    ("verify4-f32-G4-D128", "f32", 32, 8, 128, 16, [260, 1000], 4),
 ]
 
 
@@ -77,12 +86,16 @@ def test_prefill_matches_oracle(case):
     pool, _, tables, _, _ = replay(w)
     dev = build_device_batch(w)
     dev.cache_append()
-    q, qs, got = run(w, dev, m)
-    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
-    assert not np.isnan(got).any()
-    err = float(np.abs(got - ref).max())
-    say(label, f"max abs err {err:.3e}")
-    assert err <= TOL[dtype], err
+    paths = [False]
+    if pa.prefill_workspace_bytes(w.batch, hq, hkv, d, int(m.max())):
+        paths.append(True)  # the balanced split serves this size too
+    for bal in paths:
+        q, qs, got = run(w, dev, m, balanced=bal)
+        ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
+        assert not np.isnan(got).any()
+        err = float(np.abs(got - ref).max())
+        say(label, "balanced" if bal else "tiles", f"max abs err {err:.3e}")
+        assert err <= TOL[dtype], (bal, err)
 
 
 def test_one_token_chunks_equal_the_decode_bitwise():
@@ -91,11 +104,14 @@ def test_one_token_chunks_equal_the_decode_bitwise():
     dev = build_device_batch(w)
     dev.cache_append()
     m = np.ones(w.batch, dtype=np.int64)
-    q, qs, got = run(w, dev, m)
-    qd = to_device(q, w.dtype, "cuda")
-    dec = pa.decode(qd, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens, w.num_kv_heads, w.scale)
-    torch.cuda.synchronize()
-    assert np.array_equal(got, dec.float().cpu().numpy().astype(np.float64))
+    # the tile kernel sums like the single-pass decode, the balanced path like the balanced decode
+    for bal, ps in ((False, 0), (True, pa.PA_PARTITION_BALANCED)):
+        q, qs, got = run(w, dev, m, balanced=bal)
+        qd = to_device(q, w.dtype, "cuda")
+        dec = pa.decode(qd, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens, w.num_kv_heads, w.scale,
+                        partition_size=ps)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, dec.float().cpu().numpy().astype(np.float64)), bal
 
 
 def test_empty_chunks_and_error_rows_without_fault():
@@ -130,3 +146,32 @@ def test_empty_chunks_and_error_rows_without_fault():
     ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=[0, 1, 2])
     assert np.isnan(got[qs[3]:qs[4]]).all()
     assert np.abs(got[: qs[3]] - ref[: qs[3]]).max() <= 2e-2
+
+
+def test_balanced_verify_error_rows_and_workspace_reuse():
+    """The balanced path: NaN rows for impossible requests, zero-length chunks, counters left at zero."""
+    w = custom(seed=21, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+               lens=[40, 900, 5, 3000])
+    pool, _, tables, _, _ = replay(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    ws = pa.new_workspace(pa.prefill_workspace_bytes(w.batch, 32, 8, 128, 4))
+    nc = pa.lib().pa_decode_counter_bytes(w.batch, 8)
+    for m in ([4, 4, 4, 4], [3, 0, 9, 2], [1, 2, 3, 4]):
+        m = np.array(m)
+        q, qs = multi_query(w, m, seed=5)
+        out = pa.prefill(to_device(q, w.dtype, "cuda"), dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens,
+                         torch.from_numpy(qs).cuda(), w.num_kv_heads, w.scale, 4, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        ok = [b for b in range(w.batch) if m[b] <= min(4, w.seq_lens[b])]
+        ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=ok)
+        for b in range(w.batch):
+            rows = slice(qs[b], qs[b + 1])
+            if qs[b + 1] == qs[b]:
+                continue  # no new tokens: no rows
+            if b in ok:
+                assert np.abs(got[rows] - ref[rows]).max() <= 2e-2, (list(m), b)
+            else:  # 9 new tokens: more than the 4 the launch was sized for (and than the 5 cached)
+                assert np.isnan(got[rows]).all()
+        assert int(ws[:nc].cpu().view(torch.int32).abs().sum()) == 0, "counters not left at zero"
