@@ -460,8 +460,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
-              "the decode shards by sequence or KV head with no exchange, see the design notes", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path; "
+              "the decode would shard by sequence or KV head with no exchange", file=sys.stderr)
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py is a single-process, single-GPU benchmark", file=sys.stderr)
