@@ -15,8 +15,7 @@ Follows the pages:
 * "PagedAttention MCQ" page, code sketch: position ``pos`` lives in physical
   block ``table[pos // block_size]`` at offset ``pos % block_size``.
 
-Readings where the pages are silent (each is stated once more in the
-design notes):
+Readings where the pages are silent:
 
 * the free pool is a FIFO queue seeded with a given order; freed blocks
   join its tail, walked from logical block 0 upward;
