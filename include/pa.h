@@ -154,9 +154,12 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                  int32_t partition_size);
-/* Bytes at the start of the workspace that hold the balanced split's
- * counters (zero-filled once, see above). */
-size_t pa_decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads);
+/* Bytes at the start of every workspace (pa_decode, pa_prefill,
+ * pa_decode_shared_prefix) that hold the balanced split's counters
+ * (zero-filled once, see above).  The same for every call, and no call
+ * writes anything else there, so one workspace, large enough, serves calls
+ * of any size and mode one after another. */
+size_t pa_decode_counter_bytes(void);
 
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* seq_lens,
@@ -190,7 +193,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  *                passes a workspace of at least that size, 256-byte aligned,
  *                the chunks run on pa_decode's balanced split (each request's
  *                (token, head) pairs are one wave's columns); its counter
- *                bytes (pa_decode_counter_bytes) must be zero before the
+ *                bytes (pa_decode_counter_bytes()) must be zero before the
  *                first use and are left zero, as for pa_decode.  Otherwise a
  *                kernel with one wave per (kv-head, tile of query tokens,
  *                request) runs and the workspace is not used.
@@ -267,7 +270,10 @@ pa_status pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_b
  * its members' rows but reads and writes nothing outside the buffers.
  * workspace: device, 256-byte aligned, at least
  * pa_decode_shared_prefix_workspace_bytes() bytes of scratch (contents on
- * entry do not matter); calls sharing a workspace must not overlap.
+ * entry do not matter); calls sharing a workspace must not overlap.  The
+ * call leaves the first pa_decode_counter_bytes() bytes untouched, so one
+ * workspace can serve this call and pa_decode's balanced split in turn.
+ * The size function returns 0 for arguments the call would reject.
  * ------------------------------------------------------------------------ */
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                                int32_t block_size, int32_t max_blocks_per_seq,

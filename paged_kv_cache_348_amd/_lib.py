@@ -36,7 +36,7 @@ SIGNATURES = [
     ("pa_copy_blocks", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                  c_int32, c_void_p]),
     ("pa_decode_workspace_bytes", c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
-    ("pa_decode_counter_bytes", c_size_t, [c_int32, c_int32]),
+    ("pa_decode_counter_bytes", c_size_t, []),
     ("pa_decode", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                             c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                             c_void_p, c_size_t]),

@@ -323,7 +323,10 @@ __device__ __forceinline__ void count_in(const CutPiece& cp, const float* __rest
     const int ncol = MULTI ? cp.M * G : G;      // columns with an output row
     const int w0 = wave_of_step(cp.seg0, S, nw);
     const int w1 = wave_of_step(cp.seg1 - 1, S, nw);
-    int32_t* cnt = counters + (int64_t)cp.b * Hkv + cp.g;
+    // One counter per cut segment, named by the first wave holding a piece
+    // of it: a wave is the first of at most one cut segment (the last one
+    // that starts in it), so the names never collide, whatever the batch.
+    int32_t* cnt = counters + w0;
     int old = 0;
     if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0, 64);
@@ -687,9 +690,9 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Workspace layout (every mode): [counters | partials].  The counter region
-// (int32 per (sequence, kv-head), used by the balanced split) comes first so
-// that other modes never overwrite it.
-inline size_t counter_bytes(int64_t B, int64_t Hkv) { return align_up((size_t)(B * Hkv) * sizeof(int32_t)); }
+// (one int32 per wave of a balanced call) comes first and has one size for
+// every call, so that other modes and other batch sizes never overwrite it.
+inline size_t counter_bytes() { return align_up((size_t)pa::kBalancedMaxWaves * sizeof(int32_t)); }
 
 // Effective partition length and partition count of the fixed-partition modes.
 inline void partition_plan(int32_t block_size, int32_t max_blocks, int32_t partition_size, int64_t* ps,
@@ -777,7 +780,7 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq < 0 || partition_size < PA_PARTITION_BALANCED)
         return 0;
-    const size_t cnt = counter_bytes(num_seqs, num_kv_heads);
+    const size_t cnt = counter_bytes();
     if (partition_size == PA_PARTITION_BALANCED) {
         const size_t slots = 2 * (size_t)pa::kBalancedMaxWaves * (size_t)(num_q_heads / num_kv_heads);
         return cnt + align_up(slots * head_dim * sizeof(float)) + align_up(slots * 2 * sizeof(float));
@@ -828,7 +831,7 @@ extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v
         if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
             return PA_ERR_INVALID_ARG;
         char* ws = reinterpret_cast<char*>(workspace);
-        const size_t cnt = counter_bytes(num_seqs, num_kv_heads);
+        const size_t cnt = counter_bytes();
         const size_t rows = balanced ? 2 * (size_t)pa::kBalancedMaxWaves * (size_t)(num_q_heads / num_kv_heads)
                                      : (size_t)num_seqs * num_q_heads * (size_t)pmax;
         a.counters = reinterpret_cast<int32_t*>(ws);
@@ -869,7 +872,7 @@ size_t multi_balanced_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
         head_dim <= 0 || max_query_len <= 0 || (int64_t)max_query_len * (num_q_heads / num_kv_heads) > 16)
         return 0;
     const size_t slots = 2 * (size_t)pa::kBalancedMaxWaves * 16;
-    return counter_bytes(num_seqs, num_kv_heads) + align_up(slots * head_dim * sizeof(float)) +
+    return counter_bytes() + align_up(slots * head_dim * sizeof(float)) +
            align_up(slots * 2 * sizeof(float));
 }
 
@@ -882,7 +885,7 @@ pa_status multi_balanced_launch(const void* q, const void* k_cache, const void* 
                                 int32_t max_blocks_per_seq, pa_dtype dtype, void* workspace) {
     Launch a{};
     char* ws = reinterpret_cast<char*>(workspace);
-    const size_t cnt = counter_bytes(num_seqs, num_kv_heads);
+    const size_t cnt = counter_bytes();
     const size_t slots = 2 * (size_t)pa::kBalancedMaxWaves * 16;
     a.counters = reinterpret_cast<int32_t*>(ws);
     a.po = reinterpret_cast<float*>(ws + cnt);
@@ -915,7 +918,4 @@ pa_status multi_balanced_launch(const void* q, const void* k_cache, const void* 
 
 }  // namespace pa_internal
 
-extern "C" size_t pa_decode_counter_bytes(int32_t num_seqs, int32_t num_kv_heads) {
-    if (num_seqs <= 0 || num_kv_heads <= 0) return 0;
-    return counter_bytes(num_seqs, num_kv_heads);
-}
+extern "C" size_t pa_decode_counter_bytes(void) { return counter_bytes(); }

@@ -364,7 +364,10 @@ extern "C" size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int3
         return 0;
     const SharedPlan pl = shared_plan(block_size, max_blocks_per_seq, max_prefix_blocks, partition_size);
     const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)pl.p_max;
-    return align_up(rows * head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+    // [pa_decode's counter region, left untouched | partials o | partials (m, l)]:
+    // the same workspace can then serve pa_decode's balanced split as well
+    return pa_decode_counter_bytes() + align_up(rows * head_dim * sizeof(float)) +
+           align_up(rows * 2 * sizeof(float));
 }
 
 extern "C" pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
@@ -416,8 +419,9 @@ extern "C" pa_status pa_decode_shared_prefix(const void* q, const void* k_cache,
     a.groups = groups;
     a.pblk = prefix_blocks;
     a.out = out;
-    a.po = reinterpret_cast<float*>(workspace);
-    a.pml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align_up(rows * head_dim * sizeof(float)));
+    char* parts = reinterpret_cast<char*>(workspace) + pa_decode_counter_bytes();
+    a.po = reinterpret_cast<float*>(parts);
+    a.pml = reinterpret_cast<float*>(parts + align_up(rows * head_dim * sizeof(float)));
     a.B = num_seqs;
     a.Hq = num_q_heads;
     a.Hkv = num_kv_heads;

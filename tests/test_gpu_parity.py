@@ -213,11 +213,47 @@ def test_balanced_split_reuses_its_workspace_and_mixes_with_other_modes():
         outs.append((ps, host_bits(out)))
         check_out(out_f64(out), ref, w.dtype, what=f"reuse ps={ps}")
     torch.cuda.synchronize()
-    cnt = pa.lib().pa_decode_counter_bytes(w.batch, w.num_kv_heads)
+    cnt = pa.lib().pa_decode_counter_bytes()
     assert int(ws[:cnt].count_nonzero()) == 0, "counters not back to zero"
     bal = [o for ps, o in outs if ps == BAL]
     for o in bal[1:]:
         assert np.array_equal(o, bal[0]), "balanced split is not deterministic"
+
+
+def test_one_workspace_serves_calls_of_any_size():
+    """One zero-filled workspace, used by balanced calls on batches of different sizes and by a
+    shared-prefix call in between: the counters sit where no call writes anything else."""
+    small = custom(seed=31, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                   lens=[5000, 2100, 3])
+    rng = np.random.default_rng(32)
+    big = custom(seed=33, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                 lens=[int(x) for x in rng.integers(1, 1500, size=48)])
+    shared = make_workload("prefix_share", seed=34, prompts=3, samples=4, prompt_len=700, tail_max=300)
+    batches = []
+    for w in (small, big, shared):
+        pool, ref = oracle_for(w)
+        dev = build_device_batch(w)
+        dev.cache_append()
+        batches.append((w, dev, ref))
+    plan = batches[2][1].shared_plan()
+    need = max([pa.decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                          dev.max_blocks, BAL) for w, dev, _ in batches]
+               + [pa.decode_shared_prefix_workspace_bytes(shared.batch, shared.num_q_heads, shared.head_dim,
+                                                          shared.block_size, batches[2][1].max_blocks,
+                                                          plan.max_prefix_blocks, 256)])
+    ws = pa.new_workspace(need)
+    cnt = pa.lib().pa_decode_counter_bytes()
+    for i in (0, 1, 2, 0, 1, 2, 1):
+        w, dev, ref = batches[i]
+        if i == 2:
+            out = pa.decode_shared_prefix(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens,
+                                          w.num_kv_heads, w.scale, plan, partition_size=256, workspace=ws)
+        else:
+            out = pa.decode(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens, w.num_kv_heads,
+                            w.scale, partition_size=BAL, workspace=ws)
+        check_out(out_f64(out), ref, w.dtype, what=f"batch {i} (B={w.batch})")
+        torch.cuda.synchronize()
+        assert int(ws[:cnt].count_nonzero()) == 0, "counters not back to zero"
 
 
 def test_balanced_split_many_sequences():

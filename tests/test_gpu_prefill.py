@@ -156,7 +156,7 @@ def test_balanced_verify_error_rows_and_workspace_reuse():
     dev = build_device_batch(w)
     dev.cache_append()
     ws = pa.new_workspace(pa.prefill_workspace_bytes(w.batch, 32, 8, 128, 4))
-    nc = pa.lib().pa_decode_counter_bytes(w.batch, 8)
+    nc = pa.lib().pa_decode_counter_bytes()
     for m in ([4, 4, 4, 4], [3, 0, 9, 2], [1, 2, 3, 4]):
         m = np.array(m)
         q, qs = multi_query(w, m, seed=5)

@@ -72,6 +72,8 @@ CASES = [
                              block_size=8), (64,)),  # groups of 4: 32 columns at most in float32, head dim 128
     ("f32-G4-D64-bs32", dict(prompts=2, samples=16, prompt_len=170, tail_max=25, dtype="f32", num_q_heads=32,
                              head_dim=64, block_size=32), (64,)),  # 16 x 4 = 64 columns
+    # a large batch: 1040 requests in 65 groups of 16
+    ("bf16-1040-requests", dict(prompts=65, samples=16, prompt_len=40, tail_max=20), (64,)),
 ]
 
 
