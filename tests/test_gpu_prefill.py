@@ -64,6 +64,13 @@ CASES = [
     ("verify1-bf16-G16", "bf16", 16, 1, 128, 16, [100, 17, 250], 1),
     ("verify8-f32-G2-D64", "f32", 8, 4, 64, 16, [300, 77, 8], 8),
     ("verify4-f32-G4-D128", "f32", 32, 8, 128, 16, [260, 1000], 4),
+    # larger batches (8 requests, 128-256 new tokens each): many query tiles
+    # per (request, kv-head), four 16-column tiles per wave (two for float32
+    # with head dim 128)
+    ("wide4-bf16-G4", "bf16", 32, 8, 128, 16, [300, 650, 420, 512, 700, 280, 333, 600], 256),
+    ("wide2-bf16-G4-bs32", "bf16", 32, 8, 128, 32, [300, 650, 420, 512, 700, 280, 333, 600], 128),
+    ("wide2-f32-G4-D128", "f32", 32, 8, 128, 16, [200, 350, 260, 300, 410, 290, 333, 280], 128),
+    ("wide4-bf16-G8-D64", "bf16", 64, 8, 64, 16, [300, 650, 420, 512, 700, 280, 333, 600], 128),
 ]
 
 
