@@ -234,9 +234,11 @@ def prefill_main(args, w):
     out = torch.empty_like(qd)
     maxq = int(m.max())
     stream = torch.cuda.current_stream()
-    wsb = pa.prefill_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, maxq)
-    ws = pa.new_workspace(wsb) if wsb else None  # verification sizes: the balanced split's workspace, made once
-    log(f"pa_prefill path: {'balanced split' if wsb else 'query tiles'}")
+    wsb = pa.prefill_workspace_bytes(w.batch, T, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                     dev.max_blocks, maxq)
+    ws = pa.new_workspace(wsb) if wsb else None  # the faster paths' workspace, made once
+    path = pa.prefill_path(w.batch, w.num_q_heads, w.num_kv_heads, maxq, wsb)
+    log(f"pa_prefill path: {path}")
 
     def call():
         pa.prefill(qd, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens, qsd, w.num_kv_heads, w.scale, maxq,
@@ -274,7 +276,7 @@ def prefill_main(args, w):
         "config": {"workload": WORKLOAD_TEXT[args.workload] + f"; the last {args.prefill} tokens of each request "
                    "are new queries with a causal mask", "name": w.name, "seed": args.seed, "batch": w.batch,
                    "query_tokens": T, "new_tokens_per_request": args.prefill, "sum_seq_len": int(w.seq_lens.sum()),
-                   "step": "pa_prefill (" + ("balanced split" if wsb else "query tiles") + ")"},
+                   "step": f"pa_prefill ({path})"},
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm", "kernel": "pa_prefill",
             "achieved": tflops if mfma_bound else gbps, "peak": peak_tf if mfma_bound else HBM_PEAK_GBPS,

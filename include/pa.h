@@ -187,16 +187,27 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  *                0 allowed)
  *   out          device, [num_query_tokens][num_q_heads][head_dim], dtype
  *   max_query_len  >= every M_b (sizes the launch)
- *   workspace    may be NULL.  When pa_prefill_workspace_bytes() is not 0
- *                (max_query_len * (num_q_heads / num_kv_heads) <= 16 and
- *                num_seqs <= 1024: verification-sized chunks) and the caller
- *                passes a workspace of at least that size, 256-byte aligned,
- *                the chunks run on pa_decode's balanced split (each request's
- *                (token, head) pairs are one wave's columns); its counter
- *                bytes (pa_decode_counter_bytes()) must be zero before the
- *                first use and are left zero, as for pa_decode.  Otherwise a
- *                kernel with one wave per (kv-head, tile of query tokens,
- *                request) runs and the workspace is not used.
+ *   workspace    may be NULL: then a kernel with one wave per (kv-head,
+ *                tile of query tokens, request) walks all of each tile's
+ *                keys.  A caller that passes a workspace (256-byte aligned)
+ *                of at least pa_prefill_workspace_bytes() bytes, when that is
+ *                not 0, gets one of two faster paths:
+ *                - verification-sized chunks (max_query_len * (num_q_heads /
+ *                  num_kv_heads) <= 16, num_seqs <= 1024): pa_decode's
+ *                  balanced split, each request's (token, head) pairs one
+ *                  wave's columns.  Its counter bytes
+ *                  (pa_decode_counter_bytes()) must be zero before the first
+ *                  use and are left zero, as for pa_decode;
+ *                - short chunks of a batch otherwise (the tile launch would
+ *                  hold fewer than 1,024 waves and max_blocks_per_seq *
+ *                  block_size spans two 2,048-token key partitions or more):
+ *                  the tile kernel with its keys cut into partitions, whose
+ *                  partial results a merge kernel combines (log-sum-exp
+ *                  rule).  The workspace's first pa_decode_counter_bytes()
+ *                  bytes are left untouched; the rest may hold anything on
+ *                  entry.
+ *                A workspace smaller than required gives PA_ERR_INVALID_ARG.
+ *                Calls sharing a workspace must not overlap.
  *   num_q_heads / num_kv_heads <= 16; the other arguments as for pa_decode.
  * Error rows: a request with M_b > L_b, M_b > max_query_len, or L_b longer
  * than its table holds gets NaN in all its rows; a table entry outside
@@ -204,8 +215,9 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * request whose query_start pair is out of order or outside
  * [0, num_query_tokens] writes nothing.  Nothing faults.
  * ------------------------------------------------------------------------ */
-size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t max_query_len);
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int32_t max_query_len);
 
 pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                      const int32_t* seq_lens, const int32_t* query_start, int32_t num_kv_heads, float scale,

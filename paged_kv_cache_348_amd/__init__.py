@@ -31,7 +31,7 @@ __all__ = [
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
     "new_workspace", "SharedPrefixPlan", "plan_shared_prefix", "decode_shared_prefix",
     "decode_shared_prefix_workspace_bytes", "shared_prefix_max_group", "simulate_memory", "PA_MEM_CONTIGUOUS",
-    "PA_MEM_PAGED", "swap_blocks", "prefill", "prefill_workspace_bytes",
+    "PA_MEM_PAGED", "swap_blocks", "prefill", "prefill_workspace_bytes", "prefill_path",
 ]
 
 
@@ -314,10 +314,22 @@ def simulate_memory(arrival, prompt, reply, capacity_slots: int, scheme: int, pa
     return {name: int(getattr(st, name)) for name, _ in MemStats._fields_}
 
 
-def prefill_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                            max_query_len: int) -> int:
-    """Workspace for the balanced path of pa_prefill (0: that path does not apply)."""
-    return int(lib().pa_prefill_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_query_len))
+def prefill_workspace_bytes(num_seqs: int, num_query_tokens: int, num_q_heads: int, num_kv_heads: int,
+                            head_dim: int, block_size: int, max_blocks_per_seq: int, max_query_len: int) -> int:
+    """Workspace for pa_prefill's faster paths, the balanced split or key
+    partitions (0: neither applies and the tile kernel runs)."""
+    return int(lib().pa_prefill_workspace_bytes(num_seqs, num_query_tokens, num_q_heads, num_kv_heads, head_dim,
+                                                block_size, max_blocks_per_seq, max_query_len))
+
+
+def prefill_path(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_query_len: int, workspace_bytes: int) -> str:
+    """Which path pa_prefill takes given a workspace of ``workspace_bytes``
+    sized by prefill_workspace_bytes (a description for logs)."""
+    if not workspace_bytes:
+        return "query tiles"
+    if max_query_len * (num_q_heads // num_kv_heads) <= 16 and num_seqs <= 1024:
+        return "balanced split"
+    return "query tiles, key partitions"
 
 
 def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_heads: int, scale: float,
@@ -326,9 +338,10 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_hea
     holds each request's new tokens, rows query_start[b] .. query_start[b+1]-1;
     the last M_b of its seq_lens[b] cached tokens are those tokens.  Returns out [T, Hq, D].
 
-    Verification-sized chunks (max_query_len * G <= 16) run on the balanced
-    split when ``balanced`` (a zero-filled workspace is made when none is
-    given); otherwise, or with ``balanced=False``, the per-tile kernel runs."""
+    With ``balanced`` (the default) the faster paths run where they apply,
+    on ``workspace`` or on a zero-filled one made here: the balanced split for
+    verification-sized chunks (max_query_len * G <= 16), key partitions for
+    short chunks of a batch.  With ``balanced=False`` the per-tile kernel runs."""
     torch = _torch()
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     if hkv != num_kv_heads:
@@ -348,7 +361,8 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_hea
     if B == 0 or T == 0:
         return out
     ws_ptr, ws_bytes = None, 0
-    need = prefill_workspace_bytes(B, hq, hkv, d, int(max_query_len)) if balanced else 0
+    need = (prefill_workspace_bytes(B, T, hq, hkv, d, bs, block_tables.shape[1], int(max_query_len))
+            if balanced else 0)
     if need:
         if workspace is None:
             workspace = new_workspace(need, q.device)

@@ -49,7 +49,8 @@ SIGNATURES = [
     ("pa_plan_shared_prefix", c_int32, [P_I32, P_I32, c_int32, c_int32, c_int32, c_int32, c_int32, P_I32, P_I32,
                                         P_I32, P_I32, P_I32]),
     ("pa_simulate_memory", c_int32, [P_I32, P_I32, P_I32, c_int32, c_int64, c_int32, c_int32, c_void_p]),
-    ("pa_prefill_workspace_bytes", c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+    ("pa_prefill_workspace_bytes", c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                              c_int32]),
     ("pa_prefill", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                              c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                              c_int32, c_void_p, c_size_t]),

@@ -15,7 +15,15 @@
 // 128).  The wave streams the request's keys and values from position 0 to
 // its last token's position once for all columns — the same step loop as the
 // decode kernels — and each lane masks the keys past its own column's
-// position.  Every column sees key 0, so no running maximum stays -inf.
+// position.
+//
+// Key partitions: when a launch would hold few waves (short chunks of a
+// batch), its time is the longest request's walk over all its keys.  Then
+// the keys are cut into partitions of kSplitTokens; one wave per (kv-head,
+// query tile, partition, request) leaves a partial (normalised o, running
+// maximum m, sum l) per query row, and a merge kernel combines a row's
+// partials by the log-sum-exp rule.  A column with no visible key in a
+// partition leaves m = -inf, l = 0: weight 0 in the merge.
 
 #include <algorithm>
 #include <cmath>
@@ -43,16 +51,25 @@ __device__ __forceinline__ void store_row(void* __restrict__ out_, int64_t row, 
     }
 }
 
+// Key partitions (see above): rows x P partials (o: D floats, (m, l)).
+struct KeySplit {
+    int PS;  // tokens per partition; 0: no split
+    int P;   // partitions per row (grid y = query tiles x P)
+    float* o;
+    float* ml;
+};
+
 template <bool BF16, int D, int BS, int NCT>
 __global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_, const void* __restrict__ kc_,
                                                      const void* __restrict__ vc_, const int32_t* __restrict__ tables,
                                                      const int32_t* __restrict__ lens,
                                                      const int32_t* __restrict__ q_start, void* __restrict__ out_,
                                                      int T, int Hq, int Hkv, int G, int QT, int max_q,
-                                                     int max_blocks, int num_blocks, float scale_log2) {
+                                                     int max_blocks, int num_blocks, float scale_log2, KeySplit ks) {
     using C = DecodeCfg<BF16, D, BS>;
     const int g = blockIdx.x;
-    const int qt = blockIdx.y;
+    const int qt = blockIdx.y / ks.P;
+    const int p = blockIdx.y % ks.P;
     const int b = blockIdx.z;
     const int lane = threadIdx.x;
     const int n = lane & 15;
@@ -65,7 +82,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_
     if (M > max_q || M > L || (int64_t)L > (int64_t)max_blocks * BS) {
         // more query tokens than the launch bound or than cached tokens, or a
         // length the table cannot hold: tile 0 writes NaN in all the request's rows
-        if (qt != 0) return;
+        if (qt != 0 || p != 0) return;
         for (int64_t i = lane; i < (int64_t)M * G * D; i += 64) {
             const int c = (int)(i / D);
             const int64_t row = (int64_t)(t0 + c / G) * Hq + g * G + c % G;
@@ -82,6 +99,9 @@ __global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_
     const int ncol = nq * G;
     const int pos0 = L - M + q0;  // position of the tile's first query token
     const int Lend = pos0 + nq;   // keys the tile needs: [0, Lend)
+    const int kstart = p * ks.PS; // this wave's keys: [kstart, kend)
+    if (kstart >= Lend) return;
+    const int kend = ks.PS ? min(kstart + ks.PS, Lend) : Lend;
 
     typename C::QRegs qr[NCT];
     int Lcol[NCT];
@@ -91,7 +111,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_
         const char* qp = reinterpret_cast<const char*>(q_) + ((int64_t)(t0 + q0 + c / G) * Hq + g * G + c % G) * D * C::ES;
 #pragma unroll
         for (int k = 0; k < C::NKC; ++k) qr[t][k] = ld16(qp + (int64_t)(4 * k + j) * 16);
-        Lcol[t] = pos0 + c / G + 1;
+        Lcol[t] = min(pos0 + c / G + 1, kend);
     }
     RunState<BF16, D, BS> S[NCT];
 #pragma unroll
@@ -102,8 +122,8 @@ __global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_
     const char* vbase = reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES;
     const int32_t* trow = tables + (int64_t)b * max_blocks;
     bool bad = false;
-    for (int ctok = 0; ctok < Lend; ctok += kTableChunk * BS) {
-        const int cend = min(ctok + kTableChunk * BS, Lend);
+    for (int ctok = kstart; ctok < kend; ctok += kTableChunk * BS) {
+        const int cend = min(ctok + kTableChunk * BS, kend);
         const int blk0 = ctok / BS;
         const int nblk = (cend - 1) / BS - blk0 + 1;
         const int32_t ent = (lane < nblk) ? trow[blk0 + lane] : 0;
@@ -113,29 +133,106 @@ __global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_
         }
         const int nst = (cend - ctok + C::STEP - 1) / C::STEP;
         StepRegs<BF16, D, BS> cur;
-        issue_step<BF16, D, BS>(cur, kbase, vbase, blk_bytes, ent, blk0, nblk, ctok, Lend, n, j);
+        issue_step<BF16, D, BS>(cur, kbase, vbase, blk_bytes, ent, blk0, nblk, ctok, kend, n, j);
         int tok0 = ctok;
         for (int st = 0; st + 1 < nst; ++st, tok0 += C::STEP) {
             StepRegs<BF16, D, BS> nxt;
-            issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, Lend, n, j);
+            issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, kend, n, j);
             __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the compute
 #pragma unroll
             for (int t = 0; t < NCT; ++t)
-                compute_step<BF16, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, tok0, Lend, j, scale_log2,
-                                                Lcol[t], pos0 + (16 * t) / G + 1);
+                compute_step<BF16, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, tok0, kend, j, scale_log2,
+                                                Lcol[t], min(pos0 + (16 * t) / G + 1, kend));
             cur = nxt;
         }
 #pragma unroll
         for (int t = 0; t < NCT; ++t)
-            compute_step<BF16, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, tok0, Lend, j, scale_log2,
-                                            Lcol[t], pos0 + (16 * t) / G + 1);
+            compute_step<BF16, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, tok0, kend, j, scale_log2,
+                                            Lcol[t], min(pos0 + (16 * t) / G + 1, kend));
     }
+    if (ks.PS == 0) {
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) {
+            const int c = 16 * t + n;
+            if (c < ncol) {
+                const int64_t row = (int64_t)(t0 + q0 + c / G) * Hq + g * G + c % G;
+                store_row<BF16, D>(out_, row, S[t].acc, bad ? __builtin_nanf("") : 1.0f / S[t].l, j);
+            }
+        }
+        return;
+    }
+    // key partitions: the partial of each row
 #pragma unroll
     for (int t = 0; t < NCT; ++t) {
         const int c = 16 * t + n;
         if (c < ncol) {
             const int64_t row = (int64_t)(t0 + q0 + c / G) * Hq + g * G + c % G;
-            store_row<BF16, D>(out_, row, S[t].acc, bad ? __builtin_nanf("") : 1.0f / S[t].l, j);
+            const int64_t slot = row * ks.P + p;
+            const bool seen = S[t].l > 0.0f;  // a visible key in this partition
+            const float inv = bad ? __builtin_nanf("") : (seen ? 1.0f / S[t].l : 0.0f);
+#pragma unroll
+            for (int cc = 0; cc < C::NV; ++cc)
+                *reinterpret_cast<f32x4*>(ks.o + slot * D + 16 * cc + 4 * j) = S[t].acc[cc] * inv;
+            if (j == 0) {
+                ks.ml[2 * slot] = bad ? 0.0f : (seen ? S[t].m : -INFINITY);
+                ks.ml[2 * slot + 1] = bad ? 1.0f : S[t].l;
+            }
+        }
+    }
+}
+
+// The merge, on the tile kernel's grid (kv-head, query tile, request) with
+// 16 waves per workgroup, one query row per wave at a time: the same checks
+// as the tile kernel decide which tiles it wrote partials for (error rows are
+// its NaN rows, left alone here) and over how many partitions.
+template <bool BF16, int D>
+__global__ __launch_bounds__(1024) void prefill_merge_kernel(const float* __restrict__ part_o,
+                                                            const float* __restrict__ part_ml,
+                                                            const int32_t* __restrict__ lens,
+                                                            const int32_t* __restrict__ q_start,
+                                                            void* __restrict__ out_, int T, int Hq, int G, int QT,
+                                                            int max_q, int max_blocks, int BS, int PS, int P) {
+    constexpr int PER = D / 64;
+    const int g = blockIdx.x;
+    const int qt = blockIdx.y;
+    const int b = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int t0 = q_start[b];
+    const int t1 = q_start[b + 1];
+    if (t0 < 0 || t1 > T || t1 < t0) return;
+    const int M = t1 - t0;
+    const int L = lens[b];
+    if (M > max_q || M > L || (int64_t)L > (int64_t)max_blocks * BS) return;
+    const int q0 = qt * QT;
+    if (q0 >= M) return;
+    const int nq = min(QT, M - q0);
+    const int Lend = L - M + q0 + nq;
+    const int np = (Lend + PS - 1) / PS;  // partitions the tile's waves wrote
+    for (int c = wv; c < nq * G; c += 16) {
+        const int64_t row = (int64_t)(t0 + q0 + c / G) * Hq + g * G + c % G;
+        const float* ml = part_ml + row * P * 2;
+        const float* po = part_o + row * P * D + lane * PER;
+        float Mx = -INFINITY;
+        for (int i = 0; i < np; ++i) Mx = fmaxf(Mx, ml[2 * i]);
+        float num[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) num[e] = 0.0f;
+        float den = 0.0f;
+        for (int i = 0; i < np; ++i) {
+            const float w = ml[2 * i + 1] * __builtin_amdgcn_exp2f(ml[2 * i] - Mx);  // m = -inf: weight 0
+            den += w;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) num[e] += w * po[(int64_t)i * D + e];
+        }
+        const float inv = 1.0f / den;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int d = lane * PER + e;
+            if constexpr (BF16)
+                reinterpret_cast<uint16_t*>(out_)[row * D + d] = (uint16_t)bf16_bits_rne(num[e] * inv);
+            else
+                reinterpret_cast<float*>(out_)[row * D + d] = num[e] * inv;
         }
     }
 }
@@ -164,6 +261,44 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // head dim 128 (four would not fit the register file).
 constexpr int max_columns(bool bf16, int head_dim) { return (!bf16 && head_dim == 128) ? 32 : 64; }
 
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Key partitions (prefill_kernel): used when the query-tile launch would hold
+// fewer than kSplitWaves waves and the longest table spans two partitions or
+// more.  Measured on MI355X (Llama-3-8B-shaped batch, 64 requests of 512 to
+// 4,096 tokens, GQA 4): with 8 or 16 new tokens each the tile launch has 512
+// waves and its time is the 4,096-token requests' walk over all their keys;
+// partitions of 2,048 keys took it from 147 to 117 us (8 new tokens) and from
+// 252 to 164 us (16); 512 and 1,024 keys did less well.  From 32 new tokens
+// (1,024 waves) on, the partials' traffic costs more than the split saves.
+constexpr int kSplitTokens = 2048;
+constexpr int64_t kSplitWaves = 1024;
+constexpr size_t kSplitMaxBytes = size_t(1) << 30;
+
+struct SplitPlan {
+    int P;  // partitions per row (0: no split)
+    size_t o_off, ml_off, bytes;
+};
+
+// Workspace: [pa_decode's counter region, left untouched | o: rows x P x D |
+// (m, l): rows x P x 2], rows = query tokens x query heads.
+inline SplitPlan split_plan(int64_t B, int64_t T, int Hq, int Hkv, int D, int G, int maxc, int bs,
+                            int64_t max_blocks, int max_q) {
+    SplitPlan sp{0, 0, 0, 0};
+    const int QT = maxc / G;
+    const int64_t waves = (int64_t)Hkv * B * ((max_q + QT - 1) / QT);
+    const int64_t P = (max_blocks * bs + kSplitTokens - 1) / kSplitTokens;
+    if (waves >= kSplitWaves || P < 2 || T <= 0) return sp;
+    const size_t rows = (size_t)T * Hq;
+    sp.o_off = pa_decode_counter_bytes();
+    sp.ml_off = sp.o_off + align_up(rows * (size_t)P * D * sizeof(float));
+    sp.bytes = sp.ml_off + align_up(rows * (size_t)P * 2 * sizeof(float));
+    if (sp.bytes > kSplitMaxBytes) return SplitPlan{0, 0, 0, 0};
+    sp.P = (int)P;
+    return sp;
+}
+
 struct PrefillLaunch {
     const void *q, *kc, *vc;
     const int32_t *tables, *lens, *qs;
@@ -171,13 +306,20 @@ struct PrefillLaunch {
     int T, B, Hq, Hkv, G, QT, max_q, n_tiles, max_blocks, num_blocks;
     float sl2;
     hipStream_t s;
+    pa::KeySplit ks;
 };
 
 template <bool BF16, int D, int BS, int NCT>
 hipError_t launch_prefill(const PrefillLaunch& a) {
-    hipLaunchKernelGGL((pa::prefill_kernel<BF16, D, BS, NCT>), dim3((unsigned)a.Hkv, (unsigned)a.n_tiles, (unsigned)a.B),
-                       dim3(64), 0, a.s, a.q, a.kc, a.vc, a.tables, a.lens, a.qs, a.out, a.T, a.Hq, a.Hkv, a.G, a.QT,
-                       a.max_q, a.max_blocks, a.num_blocks, a.sl2);
+    hipLaunchKernelGGL((pa::prefill_kernel<BF16, D, BS, NCT>),
+                       dim3((unsigned)a.Hkv, (unsigned)(a.n_tiles * a.ks.P), (unsigned)a.B), dim3(64), 0, a.s, a.q,
+                       a.kc, a.vc, a.tables, a.lens, a.qs, a.out, a.T, a.Hq, a.Hkv, a.G, a.QT, a.max_q, a.max_blocks,
+                       a.num_blocks, a.sl2, a.ks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.ks.PS == 0) return e;
+    hipLaunchKernelGGL((pa::prefill_merge_kernel<BF16, D>), dim3((unsigned)a.Hkv, (unsigned)a.n_tiles, (unsigned)a.B),
+                       dim3(1024), 0, a.s, a.ks.o, a.ks.ml, a.lens, a.qs, a.out, a.T, a.Hq, a.G, a.QT, a.max_q,
+                       a.max_blocks, BS, a.ks.PS, a.ks.P);
     return hipGetLastError();
 }
 
@@ -199,9 +341,20 @@ hipError_t prefill_bs(int BS, int cols, const PrefillLaunch& a) {
 
 }  // namespace
 
-extern "C" size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                             int32_t head_dim, int32_t max_query_len) {
-    return pa_internal::multi_balanced_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_query_len);
+extern "C" size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                             int32_t max_blocks_per_seq, int32_t max_query_len) {
+    if (num_seqs <= 0 || num_query_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
+        max_query_len <= 0)
+        return 0;
+    const size_t bal =
+        pa_internal::multi_balanced_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_query_len);
+    if (bal) return bal;
+    const int G = num_q_heads / num_kv_heads;
+    return split_plan(num_seqs, num_query_tokens, num_q_heads, num_kv_heads, head_dim, G,
+                      max_columns(true, head_dim), block_size, max_blocks_per_seq, max_query_len)
+        .bytes;
 }
 
 extern "C" pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -256,11 +409,22 @@ extern "C" pa_status pa_prefill(const void* q, const void* k_cache, const void* 
     a.max_q = max_query_len;
     const int qt_used = std::min(a.QT, (int)max_query_len);
     a.n_tiles = (max_query_len + a.QT - 1) / a.QT;
-    if (a.n_tiles > 65535) return PA_ERR_UNSUPPORTED;
     a.max_blocks = max_blocks_per_seq;
     a.num_blocks = num_blocks;
     a.sl2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
     a.s = reinterpret_cast<hipStream_t>(stream);
+    // key partitions when the launch is small, with the caller's workspace
+    a.ks = pa::KeySplit{0, 1, nullptr, nullptr};
+    const SplitPlan sp = split_plan(num_seqs, num_query_tokens, num_q_heads, num_kv_heads, head_dim, G,
+                                    max_columns(true, head_dim), block_size, max_blocks_per_seq, max_query_len);
+    if (sp.P && workspace) {
+        if (workspace_bytes < sp.bytes || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+            return PA_ERR_INVALID_ARG;
+        char* w = reinterpret_cast<char*>(workspace);
+        a.ks = pa::KeySplit{kSplitTokens, sp.P, reinterpret_cast<float*>(w + sp.o_off),
+                            reinterpret_cast<float*>(w + sp.ml_off)};
+    }
+    if ((int64_t)a.n_tiles * a.ks.P > 65535) return PA_ERR_UNSUPPORTED;
     const int cols = qt_used * G;
     hipError_t e;
     if (dtype == PA_BF16)

@@ -439,15 +439,28 @@ def prefill_call(**kw):
     (dict(mq=0), pa.PA_OK),
     (dict(ws=fake(0x10100), wsb=16), pa.PA_ERR_INVALID_ARG),   # balanced path: workspace too small
     (dict(ws=fake(0x10010), wsb=1 << 30), pa.PA_ERR_INVALID_ARG),  # not 256-byte aligned
+    # 20 new tokens x 4 heads over tables of 200 blocks: key partitions
+    (dict(mq=20, mb=200, ws=fake(0x10100), wsb=16), pa.PA_ERR_INVALID_ARG),       # workspace too small
+    (dict(mq=20, mb=200, ws=fake(0x10010), wsb=1 << 30), pa.PA_ERR_INVALID_ARG),  # not 256-byte aligned
 ])
 def test_prefill_rejects_bad_arguments(kw, expect):
     assert prefill_call(**kw) == expect
 
 
 def test_prefill_workspace_size():
+    cnt = _l().pa_decode_counter_bytes()
+    # arguments: B, T, Hq, Hkv, D, block size, table width, max new tokens
     # 4 new tokens x 4 heads = 16 columns: the balanced path, with counters and 16-column slots
-    n = pa.prefill_workspace_bytes(64, 32, 8, 128, 4)
-    assert n >= _l().pa_decode_counter_bytes() + 2 * 2048 * 16 * 130 * 4 and n % 256 == 0
-    assert pa.prefill_workspace_bytes(64, 32, 8, 128, 5) == 0   # 20 columns: the tile kernel
-    assert pa.prefill_workspace_bytes(1025, 32, 8, 128, 4) == 0
-    assert pa.prefill_workspace_bytes(8, 8, 8, 64, 16) > 0      # G = 1: 16 tokens
+    n = pa.prefill_workspace_bytes(64, 256, 32, 8, 128, 16, 256, 4)
+    assert n >= cnt + 2 * 2048 * 16 * 130 * 4 and n % 256 == 0
+    assert pa.prefill_workspace_bytes(8, 128, 8, 8, 64, 16, 256, 16) > 0  # G = 1: 16 tokens
+    # 5 new tokens x 4 heads = 20 columns: 512 tile waves over tables of 4096 tokens, so
+    # 2 key partitions: per query row 2 partials of D + 2 floats
+    n = pa.prefill_workspace_bytes(64, 320, 32, 8, 128, 16, 256, 5)
+    rows = 320 * 32
+    assert n >= cnt + rows * 2 * 130 * 4 and n % 256 == 0
+    assert pa.prefill_workspace_bytes(64, 320, 32, 8, 128, 16, 128, 5) == 0     # one partition: tiles only
+    assert pa.prefill_workspace_bytes(64, 2048, 32, 8, 128, 16, 256, 32) == 0   # 1,024 tile waves
+    assert pa.prefill_workspace_bytes(64, 32768, 32, 8, 128, 16, 256, 512) == 0  # 16,384 tile waves
+    assert pa.prefill_workspace_bytes(1025, 4100, 32, 8, 128, 16, 256, 4) == 0   # many waves already
+    assert pa.prefill_workspace_bytes(64, 320, 32, 7, 128, 16, 256, 5) == 0      # Hq not a multiple of Hkv

@@ -3,7 +3,8 @@
 Verification-sized chunks (a few tokens), chunked prefill and full prefill,
 group sizes 1..16, head dims 64 and 128, every block size, float32 and
 bfloat16, several query tiles per request, keys spanning several table
-chunks, empty chunks, and the documented error rows (more new tokens than
+chunks and several key partitions (merged by the log-sum-exp rule), empty
+chunks, and the documented error rows (more new tokens than
 cached ones, more than the launch bound, a bad table entry) — within 1e-5
 (float32) / 2e-2 (bfloat16) of the float64 oracle, NaN only where promised.
 """
@@ -64,6 +65,15 @@ CASES = [
     ("verify1-bf16-G16", "bf16", 16, 1, 128, 16, [100, 17, 250], 1),
     ("verify8-f32-G2-D64", "f32", 8, 4, 64, 16, [300, 77, 8], 8),
     ("verify4-f32-G4-D128", "f32", 32, 8, 128, 16, [260, 1000], 4),
+    # key partitions (2,048 keys each) where the tables span two or more:
+    # query tokens straddling a partition boundary (some columns see no key of
+    # a partition), full prefill past one partition, several partitions
+    ("split-bf16-G4-straddle", "bf16", 32, 8, 128, 16, [1100, 2100, 3000, 40], 100),
+    ("split-bf16-G8-bs32", "bf16", 64, 8, 128, 32, [2500, 1030, 700], 33),
+    ("split-bf16-G1-bs8-D64", "bf16", 8, 8, 64, 8, [1500, 2049, 90], 40),
+    ("split-bf16-full", "bf16", 4, 1, 128, 16, [2300], "L"),
+    ("split-f32-G4-D128", "f32", 32, 8, 128, 16, [2200, 1400], 24),
+    ("split-f32-G2-D64-bs32", "f32", 8, 4, 64, 32, [3100, 1024, 1025], 9),
     # larger batches (8 requests, 128-256 new tokens each): many query tiles
     # per (request, kv-head), four 16-column tiles per wave (two for float32
     # with head dim 128)
@@ -94,15 +104,17 @@ def test_prefill_matches_oracle(case):
     dev = build_device_batch(w)
     dev.cache_append()
     paths = [False]
-    if pa.prefill_workspace_bytes(w.batch, hq, hkv, d, int(m.max())):
-        paths.append(True)  # the balanced split serves this size too
+    wsb = pa.prefill_workspace_bytes(w.batch, int(m.sum()), hq, hkv, d, bs, dev.max_blocks, int(m.max()))
+    if wsb:
+        paths.append(True)  # the balanced split or key partitions serve this size too
     for bal in paths:
         q, qs, got = run(w, dev, m, balanced=bal)
         ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
         assert not np.isnan(got).any()
         err = float(np.abs(got - ref).max())
-        say(label, "balanced" if bal else "tiles", f"max abs err {err:.3e}")
-        assert err <= TOL[dtype], (bal, err)
+        path = pa.prefill_path(w.batch, hq, hkv, int(m.max()), wsb if bal else 0)
+        say(label, path, f"max abs err {err:.3e}")
+        assert err <= TOL[dtype], (path, err)
 
 
 def test_one_token_chunks_equal_the_decode_bitwise():
@@ -162,7 +174,7 @@ def test_balanced_verify_error_rows_and_workspace_reuse():
     pool, _, tables, _, _ = replay(w)
     dev = build_device_batch(w)
     dev.cache_append()
-    ws = pa.new_workspace(pa.prefill_workspace_bytes(w.batch, 32, 8, 128, 4))
+    ws = pa.new_workspace(pa.prefill_workspace_bytes(w.batch, 16, 32, 8, 128, 16, dev.max_blocks, 4))
     nc = pa.lib().pa_decode_counter_bytes()
     for m in ([4, 4, 4, 4], [3, 0, 9, 2], [1, 2, 3, 4]):
         m = np.array(m)
@@ -182,3 +194,44 @@ def test_balanced_verify_error_rows_and_workspace_reuse():
             else:  # 9 new tokens: more than the 4 the launch was sized for (and than the 5 cached)
                 assert np.isnan(got[rows]).all()
         assert int(ws[:nc].cpu().view(torch.int32).abs().sum()) == 0, "counters not left at zero"
+
+
+def test_key_partitions_error_rows_and_workspace_reuse():
+    """Key partitions: NaN rows only where promised (more new tokens than cached ones or
+    than the launch bound, a bad table entry in a later partition), the other rows right,
+    on one workspace reused by calls of different sizes."""
+    w = custom(seed=23, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+               lens=[2100, 1500, 9, 3000])
+    pool, _, tables, _, _ = replay(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    big = pa.prefill_workspace_bytes(w.batch, 4 * 40, 32, 8, 128, 16, dev.max_blocks, 40)
+    assert big > 0
+    ws = pa.new_workspace(big)
+    for m, max_q, tb, bad_rows in (([40, 7, 9, 33], 40, None, []),  # request 2: all 9 tokens new
+                                   ([30, 12, 0, 25], 30, None, []),
+                                   ([40, 12, 20, 33], 40, None, [2]),  # 20 new tokens, 9 cached
+                                   ([20, 12, 5, 33], 25, None, [3]),   # 33 new tokens, launch sized for 25
+                                   ([20, 12, 5, 18], 25, (3, 150), [3])):  # bad entry among keys 2400..2415
+        m = np.array(m)
+        tbd = dev.block_tables
+        if tb is not None:
+            tbd = tbd.clone()
+            tbd[tb[0], tb[1]] = w.num_blocks + 5
+        q, qs = multi_query(w, m, seed=7)
+        assert pa.prefill_path(w.batch, 32, 8, max_q, big) == "query tiles, key partitions"
+        out = pa.prefill(to_device(q, w.dtype, "cuda"), dev.k_cache, dev.v_cache, tbd, dev.seq_lens,
+                         torch.from_numpy(qs).cuda(), w.num_kv_heads, w.scale, max_q, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        ok = [b for b in range(w.batch) if b not in bad_rows]
+        ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=ok)
+        say("partitions", list(m), "max_q", max_q, "NaN requests", bad_rows)
+        for b in range(w.batch):
+            rows = slice(qs[b], qs[b + 1])
+            if qs[b + 1] == qs[b]:
+                continue
+            if b in ok:
+                assert np.abs(got[rows] - ref[rows]).max() <= 2e-2, (list(m), b)
+            else:
+                assert np.isnan(got[rows]).all(), (list(m), b)
