@@ -116,12 +116,18 @@ __global__ __launch_bounds__(64) void decode_kernel(
 }
 
 // Log-sum-exp merge of per-partition results: one 256-lane workgroup per
-// (query head, sequence); wave w takes partitions w, w+4, ...
+// (query head, sequence).  A lane owns four consecutive head-dim elements of
+// one partition row at a time (D / 4 lanes per row, so 1024 / D rows side by
+// side) and takes four rows per loop trip with their loads issued together,
+// so a workgroup has up to 4096 / D partition rows in flight; the row
+// groups' sums meet in LDS.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     const int32_t* __restrict__ lens, void* __restrict__ out_,
                                                     int Hq, int max_blocks, int BS, int PS, int P_max) {
+    constexpr int LPR = D / 4;     // lanes per partition row
+    constexpr int RG = 256 / LPR;  // partition rows side by side
     const int h = blockIdx.x;
     const int b = blockIdx.y;
     const int L = lens[b];
@@ -131,39 +137,61 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     const int64_t row = (int64_t)b * Hq + h;
     const float* ml = part_ml + row * P_max * 2;
     const float* po = part_o + row * P_max * D;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int rg = t / LPR;
+    const int c = t % LPR;
 
     float M = -INFINITY;
     for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[2 * i]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
 
-    constexpr int PER = D / 64;
-    float num[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int i = w; i < np; i += 4) {
-        const float wt = ml[2 * i + 1] * __builtin_amdgcn_exp2f(ml[2 * i] - M);
-        den += wt;
+    int i = rg;
+    for (; i + 3 * RG < np; i += 4 * RG) {
+        float2 w[4];
+        f32x4 o[4];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) num[e] += wt * po[(int64_t)i * D + lane * PER + e];
+        for (int u = 0; u < 4; ++u) {
+            w[u] = *reinterpret_cast<const float2*>(ml + 2 * (i + u * RG));
+            o[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(i + u * RG) * D + 4 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float wt = w[u].y * __builtin_amdgcn_exp2f(w[u].x - M);
+            den += wt;
+            num += wt * o[u];
+        }
     }
-    __shared__ float s_num[4][D];
-    __shared__ float s_den[4];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) s_num[w][lane * PER + e] = num[e];
-    if (lane == 0) s_den[w] = den;
+    for (; i < np; i += RG) {
+        const float2 w = *reinterpret_cast<const float2*>(ml + 2 * i);
+        const float wt = w.y * __builtin_amdgcn_exp2f(w.x - M);
+        den += wt;
+        num += wt * *reinterpret_cast<const f32x4*>(po + (int64_t)i * D + 4 * c);
+    }
+    __shared__ f32x4 s_num[RG][LPR];
+    __shared__ float s_den[RG];
+    s_num[rg][c] = num;
+    if (c == 0) s_den[rg] = den;
     __syncthreads();
-    if (threadIdx.x < D) {
-        const int d = threadIdx.x;
-        const float total = s_den[0] + s_den[1] + s_den[2] + s_den[3];
-        const float v = (s_num[0][d] + s_num[1][d] + s_num[2][d] + s_num[3][d]) / total;
-        if constexpr (BF16)
-            reinterpret_cast<uint16_t*>(out_)[row * D + d] = (uint16_t)bf16_bits_rne(v);
-        else
-            reinterpret_cast<float*>(out_)[row * D + d] = v;
+    if (t < LPR) {
+        f32x4 v = s_num[0][t];
+        float total = s_den[0];
+#pragma unroll
+        for (int r = 1; r < RG; ++r) {
+            v += s_num[r][t];
+            total += s_den[r];
+        }
+        v = v / total;
+        if constexpr (BF16) {
+            const uint32_t lo = pack_bf16x2(v[0], v[1]);
+            const uint32_t hi = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out_) + row * D + 4 * t) = u32x2{lo, hi};
+        } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out_) + row * D + 4 * t) = v;
+        }
     }
 }
 
