@@ -189,7 +189,12 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  *   max_query_len  >= every M_b (sizes the launch)
  *   workspace    may be NULL: then a kernel with one wave per (kv-head,
  *                tile of query tokens, request) walks all of each tile's
- *                keys.  A caller that passes a workspace (256-byte aligned)
+ *                keys; for bfloat16 chunks of max_query_len * (num_q_heads /
+ *                num_kv_heads) >= 128 columns, workgroups of four such tiles
+ *                walk them together, each key/value step read from the pool
+ *                once and shared through LDS.  The same holds with a
+ *                workspace when neither path below applies (see
+ *                pa_prefill_workspace_bytes).  A caller that passes a workspace (256-byte aligned)
  *                of at least pa_prefill_workspace_bytes() bytes, when that is
  *                not 0, gets one of two faster paths:
  *                - verification-sized chunks (max_query_len * (num_q_heads /
@@ -211,7 +216,8 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  *   num_q_heads / num_kv_heads <= 16; the other arguments as for pa_decode.
  * Error rows: a request with M_b > L_b, M_b > max_query_len, or L_b longer
  * than its table holds gets NaN in all its rows; a table entry outside
- * [0, num_blocks) among a query tile's keys gives NaN rows for that tile; a
+ * [0, num_blocks) among a query tile's keys gives NaN rows for that tile
+ * (for all four tiles of a workgroup on the workgroup path); a
  * request whose query_start pair is out of order or outside
  * [0, num_query_tokens] writes nothing.  Nothing faults.
  * ------------------------------------------------------------------------ */

@@ -322,10 +322,18 @@ def prefill_workspace_bytes(num_seqs: int, num_query_tokens: int, num_q_heads: i
                                                 block_size, max_blocks_per_seq, max_query_len))
 
 
-def prefill_path(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_query_len: int, workspace_bytes: int) -> str:
+# bfloat16 chunks of at least this many (token, head) columns run on
+# workgroups of four query tiles sharing each key/value step through LDS
+PREFILL_WORKGROUP_COLUMNS = 128
+
+
+def prefill_path(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_query_len: int, workspace_bytes: int,
+                 bf16: bool = True) -> str:
     """Which path pa_prefill takes given a workspace of ``workspace_bytes``
     sized by prefill_workspace_bytes (a description for logs)."""
     if not workspace_bytes:
+        if bf16 and max_query_len * (num_q_heads // num_kv_heads) >= PREFILL_WORKGROUP_COLUMNS:
+            return "workgroup tiles"
         return "query tiles"
     if max_query_len * (num_q_heads // num_kv_heads) <= 16 and num_seqs <= 1024:
         return "balanced split"
@@ -341,7 +349,9 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_hea
     With ``balanced`` (the default) the faster paths run where they apply,
     on ``workspace`` or on a zero-filled one made here: the balanced split for
     verification-sized chunks (max_query_len * G <= 16), key partitions for
-    short chunks of a batch.  With ``balanced=False`` the per-tile kernel runs."""
+    short chunks of a batch.  With ``balanced=False`` (or where neither
+    applies) the query-tile kernel runs, or for bfloat16 chunks of at least
+    PREFILL_WORKGROUP_COLUMNS (token, head) columns the workgroup kernel."""
     torch = _torch()
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     if hkv != num_kv_heads:

@@ -33,14 +33,17 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict
     const int64_t th = idx / C;  // token * Hkv + head
     const int h = (int)(th % Hkv);
     const int64_t t = th / Hkv;
+    // the token's chunks are loaded together with its slot (their addresses
+    // do not depend on it), so the launch waits one memory round trip
+    const int64_t src = (th * D + (int64_t)c * X) * ES;
+    const u32x4 kv = ld16(k + src);
+    const u32x4 vv = ld16(v + src);
     const int64_t s = slots[t];
     if (s < 0 || s >= total_slots) return;
     const int64_t blk = s / BS;
     const int off = (int)(s % BS);
     const int64_t tile = (blk * Hkv + h) * (int64_t)D * BS;  // element offset of the (block, head) tile
-    const int64_t src = (th * D + (int64_t)c * X) * ES;
-    st16(kc + (tile + ((int64_t)c * BS + off) * X) * ES, ld16(k + src));
-    const u32x4 vv = ld16(v + src);
+    st16(kc + (tile + ((int64_t)c * BS + off) * X) * ES, kv);
     if constexpr (ES == 2) {
         // bf16 blocks of 16 or 32 tokens store values with bits 2 and 3 of the
         // in-block offset swapped (include/pa.h)

@@ -237,6 +237,267 @@ __global__ __launch_bounds__(1024) void prefill_merge_kernel(const float* __rest
     }
 }
 
+// ---------------------------------------------------------------------------- workgroup tiles (bfloat16)
+//
+// Long chunks.  A workgroup of NW waves takes NW consecutive wave tiles of query tokens of one (kv-head, request) — each
+// wave NCT 16-column matrix-core tiles of (token, head) columns, as in
+// prefill_kernel — and walks the keys once for all of them, up to its last
+// token's position.  Every 32-token step of keys and values is copied from
+// the pool into a two-slot LDS ring by all the workgroup's lanes: a lane's
+// 16-byte pieces of a step are loaded two steps ahead into registers (the
+// block-table entries they need one load earlier still, so waiting for an
+// entry never waits for the step just issued), and written to the ring one
+// step ahead; the waves read their operands from the ring in the order
+// prefill_kernel reads them from the pool.  One barrier per step separates
+// the writes into a slot from the reads of the step before.  A step's keys
+// and values are read from the pool once per workgroup instead of once per
+// wave.
+
+template <int D, int BS, int NW>
+struct FlashCfg {
+    static constexpr int TILE = D * BS * 2;  // bytes of one (block, head) tile
+    static constexpr int PAD = 128;          // LDS gap after each tile (the two tiles a lane group reads differ in bank)
+    static constexpr int TSTRIDE = TILE + PAD;
+    static constexpr int NE = 32 / BS;       // blocks of one step
+    static constexpr int SLOT = NE * TSTRIDE;  // LDS bytes of a step's keys (or values)
+    static constexpr int NLD = 32 * D * 2 / (1024 * NW);  // 16-byte pieces per lane of a step's keys
+    static_assert(NLD >= 1 && NLD * 1024 * NW == 32 * D * 2 && TILE % 1024 == 0,
+                  "the waves' pieces cover a step, and one wave's piece lies in one tile");
+    // piece i of wave w: bytes [1024 (w + NW i), +1024) of the step's keys
+    // (values), in tile blk(w, i) of the step
+    __device__ static int blk(int w, int i) { return 1024 * (w + NW * i) / TILE; }
+    __device__ static int inner(int w, int i) { return 1024 * (w + NW * i) - blk(w, i) * TILE; }
+};
+
+template <int NLD>
+struct FlashStage {
+    u32x4 k[NLD];
+    u32x4 v[NLD];
+};
+
+template <int NLD>
+struct FlashEnt {
+    int32_t e[NLD];
+};
+
+// Operands of one step (tokens tok0 .. tok0 + 31, clamped to last) from an
+// LDS slot holding the step's tiles; the same placement as issue_step_e.
+template <int D, int BS, int TSTRIDE>
+__device__ __forceinline__ void flash_read_step(StepRegs<true, D, BS>& r, const char* sk, const char* sv, int tok0,
+                                                int last, int n, int j) {
+    using C = DecodeCfg<true, D, BS>;
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+        const int srow = C::VIL ? 16 * (n >> 3) + 8 * t + (n & 7) : 16 * t + n;
+        const int tok = min(tok0 + srow, last);
+        const char* kp = sk + (tok / BS - tok0 / BS) * TSTRIDE + (tok % BS) * 16;
+#pragma unroll
+        for (int c = 0; c < C::NKC; ++c) r.k[t][c] = *reinterpret_cast<const u32x4*>(kp + (4 * c + j) * BS * 16);
+    }
+    if constexpr (C::VIL) {
+        const int tv = (tok0 + 16 * (j >> 1) <= last) ? tok0 + 8 * j : (last & ~7);
+        const char* vp = sv + (tv / BS - tok0 / BS) * TSTRIDE + (tv % BS) * 2;
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) r.v[c] = *reinterpret_cast<const u32x4*>(vp + (16 * c + n) * BS * 2);
+    } else {
+        const int ta = min(tok0 + 4 * j, last & ~3);
+        const int tb = min(tok0 + 16 + 4 * j, last & ~3);
+        const char* va = sv + (ta / BS - tok0 / BS) * TSTRIDE + (ta % BS) * 2;
+        const char* vb = sv + (tb / BS - tok0 / BS) * TSTRIDE + (tb % BS) * 2;
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) {
+            const int d = 16 * c + n;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(va + d * BS * 2);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vb + d * BS * 2);
+            r.v[c] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    }
+}
+
+template <int D, int BS, int NW, int NCT>
+struct FlashWave {
+    using C = DecodeCfg<true, D, BS>;
+    using F = FlashCfg<D, BS, NW>;
+    using Stage = FlashStage<F::NLD>;
+    using Ent = FlashEnt<F::NLD>;
+    char* lds;  // two slots of [keys SLOT | values SLOT]
+    const char* kbase;
+    const char* vbase;
+    const int32_t* trow;
+    int64_t blk_bytes;
+    int num_blocks, lastb, nst, kend, w, lane, n, j;
+    float sl2;
+    bool bad;
+    int Lcol[NCT], Lmin[NCT];
+    u32x4 qr[NCT][C::NKC];
+    RunState<true, D, BS> S[NCT];
+
+    // table entries of this lane's pieces of step y (vector loads: their wait
+    // is ordered with the key/value loads, see above)
+    __device__ __forceinline__ void ent(Ent& E, int y) {
+#pragma unroll
+        for (int i = 0; i < F::NLD; ++i) E.e[i] = trow[min(y * 32 / BS + F::blk(w, i), lastb)];
+    }
+    __device__ __forceinline__ void issue(Stage& R, const Ent& E) {
+#pragma unroll
+        for (int i = 0; i < F::NLD; ++i) {
+            const int32_t e = E.e[i];
+            const bool ok = e >= 0 && e < num_blocks;
+            bad |= !ok;
+            const int64_t off = (int64_t)(ok ? e : 0) * blk_bytes + F::inner(w, i) + 16 * lane;
+            R.k[i] = ld16(kbase + off);
+            R.v[i] = ld16(vbase + off);
+        }
+    }
+    __device__ __forceinline__ void put(const Stage& R, int slot) {
+        char* sk = lds + slot * 2 * F::SLOT;
+#pragma unroll
+        for (int i = 0; i < F::NLD; ++i) {
+            const int o = F::blk(w, i) * F::TSTRIDE + F::inner(w, i) + 16 * lane;
+            *reinterpret_cast<u32x4*>(sk + o) = R.k[i];
+            *reinterpret_cast<u32x4*>(sk + F::SLOT + o) = R.v[i];
+        }
+    }
+    __device__ __forceinline__ void compute(int x, int slot) {
+        StepRegs<true, D, BS> cur;
+        const char* sk = lds + slot * 2 * F::SLOT;
+        flash_read_step<D, BS, F::TSTRIDE>(cur, sk, sk + F::SLOT, 32 * x, kend - 1, n, j);
+#pragma unroll
+        for (int t = 0; t < NCT; ++t)
+            compute_step<true, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, 32 * x, kend, j, sl2, Lcol[t],
+                                            Lmin[t]);
+    }
+    // step x of the loop; Sn holds step x + 1, En the entries of step x + 3,
+    // Ex is free for step x + 4's entries.  Loads and ring writes happen
+    // whether or not their step exists (past the last step the entries repeat
+    // the last block, and a slot written past the end is never read): the
+    // same sequence of memory operations on every path lets each wait leave
+    // the later steps' loads in flight.
+    __device__ __forceinline__ void step(int x, int slot, Stage& Sn, Ent& Ex,
+                                         const Ent& En) {
+        if (x < nst) compute(x, slot);  // (the pair loop's extra step computes nothing)
+        put(Sn, slot ^ 1);
+        __syncthreads();
+        ent(Ex, x + 4);
+        __builtin_amdgcn_sched_barrier(0);  // the entries are issued before the step that does not need them
+        issue(Sn, En);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+};
+
+template <int D, int BS, int NW, int NCT, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
+void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ kc_, const void* __restrict__ vc_,
+                          const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+                          const int32_t* __restrict__ q_start, void* __restrict__ out_, int T, int Hq, int Hkv,
+                          int G, int QTw, int max_q, int max_blocks, int num_blocks, float scale_log2) {
+    using C = DecodeCfg<true, D, BS>;
+    using F = FlashCfg<D, BS, NW>;
+    using W_t = FlashWave<D, BS, NW, NCT>;
+    __shared__ __attribute__((aligned(16))) char lds[4 * F::SLOT];
+    __shared__ int s_bad;
+    const int g = blockIdx.x;
+    const int qt = blockIdx.y;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int t0 = q_start[b];
+    const int t1 = q_start[b + 1];
+    if (t0 < 0 || t1 > T || t1 < t0) return;  // malformed query offsets: the request writes nothing
+    const int M = t1 - t0;
+    const int L = lens[b];
+    if (M > max_q || M > L || (int64_t)L > (int64_t)max_blocks * BS) {
+        // as prefill_kernel: the first tile writes NaN in all the request's rows
+        if (qt != 0) return;
+        for (int64_t i = tid; i < (int64_t)M * G * D; i += 64 * NW) {
+            const int c = (int)(i / D);
+            const int64_t row = (int64_t)(t0 + c / G) * Hq + g * G + c % G;
+            reinterpret_cast<uint16_t*>(out_)[row * D + i % D] = (uint16_t)bf16_bits_rne(__builtin_nanf(""));
+        }
+        return;
+    }
+    const int QTW = QTw * NW;  // query tokens of the workgroup
+    const int q0 = qt * QTW;
+    if (q0 >= M) return;
+    const int kend = L - M + q0 + min(QTW, M - q0);  // keys of the workgroup: [0, kend)
+
+    W_t W;
+    W.lds = lds;
+    W.w = tid >> 6;
+    W.lane = tid & 63;
+    W.n = W.lane & 15;
+    W.j = W.lane >> 4;
+    W.blk_bytes = (int64_t)Hkv * C::TILE * C::ES;
+    W.kbase = reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES;
+    W.vbase = reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES;
+    W.trow = tables + (int64_t)b * max_blocks;
+    W.num_blocks = num_blocks;
+    W.kend = kend;
+    W.lastb = (kend - 1) / BS;
+    W.nst = (kend + 31) / 32;
+    W.sl2 = scale_log2;
+    W.bad = false;
+    if (tid == 0) s_bad = 0;
+
+    // this wave's query tokens and columns (padding columns repeat the last
+    // real one; a wave past the request's tokens computes column 0's and
+    // stores nothing)
+    const int qw = q0 + W.w * QTw;                 // first query token of the wave
+    const int nqw = max(0, min(QTw, M - qw));      // its tokens
+    const int ncol = nqw * G;
+    const int pos0 = L - M + qw;
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) {
+        const int c = max(0, min(16 * t + W.n, ncol - 1));
+        const int tok = nqw > 0 ? qw + c / G : q0;
+        const int head = nqw > 0 ? c % G : 0;
+        const char* qp = reinterpret_cast<const char*>(q_) + ((int64_t)(t0 + tok) * Hq + g * G + head) * D * 2;
+#pragma unroll
+        for (int k = 0; k < C::NKC; ++k) W.qr[t][k] = ld16(qp + (int64_t)(4 * k + W.j) * 16);
+        W.Lcol[t] = min(L - M + tok + 1, kend);
+        W.Lmin[t] = nqw > 0 ? min(pos0 + (16 * t) / G + 1, kend) : W.Lcol[t];
+        run_init(W.S[t]);
+    }
+
+    // prologue: step 0 in slot 0, steps 1 and 2 in flight, step 3's entries
+    // in flight (steps past the last one load the last block again)
+    typename W_t::Stage SA, SB;
+    typename W_t::Ent EA, EB;
+    const int nst = W.nst;
+    W.ent(EA, 0);
+    W.ent(EB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    W.issue(SA, EA);
+    __builtin_amdgcn_sched_barrier(0);
+    W.ent(EA, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    W.issue(SB, EB);
+    __builtin_amdgcn_sched_barrier(0);
+    W.ent(EB, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    W.put(SA, 0);
+    __syncthreads();
+    W.issue(SA, EA);
+    __builtin_amdgcn_sched_barrier(0);
+    // steps in pairs; an odd count ends with one step past the keys, which
+    // only keeps the loads and ring writes in step
+    for (int x = 0; x < nst; x += 2) {
+        W.step(x, 0, SB, EA, EB);
+        W.step(x + 1, 1, SA, EB, EA);
+    }
+
+    if (W.bad) s_bad = 1;
+    __syncthreads();
+    const bool bad = s_bad != 0;
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) {
+        const int c = 16 * t + W.n;
+        if (c < ncol) {
+            const int64_t row = (int64_t)(t0 + qw + c / G) * Hq + g * G + c % G;
+            store_row<true, D>(out_, row, W.S[t].acc, bad ? __builtin_nanf("") : 1.0f / W.S[t].l, W.j);
+        }
+    }
+}
+
 }  // namespace pa
 
 // ---------------------------------------------------------------------------- host side
@@ -321,6 +582,37 @@ hipError_t launch_prefill(const PrefillLaunch& a) {
                        dim3(1024), 0, a.s, a.ks.o, a.ks.ml, a.lens, a.qs, a.out, a.T, a.Hq, a.G, a.QT, a.max_q,
                        a.max_blocks, BS, a.ks.PS, a.ks.P);
     return hipGetLastError();
+}
+
+// Workgroup tiles for bfloat16 chunks (prefill_flash_kernel): kFlashCols
+// columns per wave, two waves per SIMD (the register budget that allows),
+// flash_waves<D>() waves per workgroup.
+constexpr int kFlashCols = 32;
+constexpr int kFlashWavesPerSimd = 2;
+constexpr int kFlashWavesD128 = 4;
+template <int D>
+constexpr int flash_waves() { return D == 128 ? kFlashWavesD128 : 4; }
+inline int flash_waves(int D) { return D == 128 ? flash_waves<128>() : flash_waves<64>(); }
+
+template <int D, int BS>
+hipError_t launch_flash(const PrefillLaunch& a) {
+    constexpr int NW = flash_waves<D>();
+    const int QTw = kFlashCols / a.G;
+    const int QTW = QTw * NW;
+    hipLaunchKernelGGL((pa::prefill_flash_kernel<D, BS, NW, kFlashCols / 16, kFlashWavesPerSimd>),
+                       dim3((unsigned)a.Hkv, (unsigned)((a.max_q + QTW - 1) / QTW), (unsigned)a.B), dim3(64 * NW), 0,
+                       a.s, a.q, a.kc, a.vc, a.tables, a.lens, a.qs, a.out, a.T, a.Hq, a.Hkv, a.G, QTw, a.max_q,
+                       a.max_blocks, a.num_blocks, a.sl2);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t flash_bs(int BS, const PrefillLaunch& a) {
+    switch (BS) {
+        case 8: return launch_flash<D, 8>(a);
+        case 16: return launch_flash<D, 16>(a);
+        default: return launch_flash<D, 32>(a);
+    }
 }
 
 template <bool BF16, int D, int BS>
@@ -427,6 +719,12 @@ extern "C" pa_status pa_prefill(const void* q, const void* k_cache, const void* 
     if ((int64_t)a.n_tiles * a.ks.P > 65535) return PA_ERR_UNSUPPORTED;
     const int cols = qt_used * G;
     hipError_t e;
+    if (dtype == PA_BF16 && a.ks.PS == 0 &&
+        (int64_t)max_query_len * G >= (int64_t)kFlashCols * flash_waves(head_dim)) {
+        // chunks that fill a workgroup's tiles: workgroup tiles sharing each step through LDS
+        e = head_dim == 128 ? flash_bs<128>(block_size, a) : flash_bs<64>(block_size, a);
+        return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    }
     if (dtype == PA_BF16)
         e = head_dim == 128 ? prefill_bs<true, 128>(block_size, cols, a) : prefill_bs<true, 64>(block_size, cols, a);
     else

@@ -112,7 +112,7 @@ def test_prefill_matches_oracle(case):
         ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
         assert not np.isnan(got).any()
         err = float(np.abs(got - ref).max())
-        path = pa.prefill_path(w.batch, hq, hkv, int(m.max()), wsb if bal else 0)
+        path = pa.prefill_path(w.batch, hq, hkv, int(m.max()), wsb if bal else 0, bf16=dtype == "bf16")
         say(label, path, f"max abs err {err:.3e}")
         assert err <= TOL[dtype], (path, err)
 
@@ -165,6 +165,48 @@ def test_empty_chunks_and_error_rows_without_fault():
     ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=[0, 1, 2])
     assert np.isnan(got[qs[3]:qs[4]]).all()
     assert np.abs(got[: qs[3]] - ref[: qs[3]]).max() <= 2e-2
+
+
+@pytest.mark.parametrize("bs,hq,d", [(8, 32, 128), (16, 64, 128), (32, 16, 64)])
+def test_workgroup_tiles_error_rows_without_fault(bs, hq, d):
+    """Chunks long enough for the workgroup path: odd and even step counts,
+    waves past a request's tokens, then the error rows (too many new tokens,
+    the launch bound, a bad table entry) fall on whole workgroups only."""
+    hkv = 8 if hq >= 32 else 1
+    g = hq // hkv
+    w = custom(seed=40 + bs, dtype="bf16", num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+               lens=[300, 517, 96, 900, 70])
+    pool, _, tables, _, _ = replay(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    m = np.array([257, 100, 96, 33, 64])
+    assert pa.prefill_path(w.batch, hq, hkv, int(m.max()), 0) == "workgroup tiles"
+    say("workgroup tiles", "bs", bs, "G", g, "D", d, "M", list(m))
+    q, qs, got = run(w, dev, m, balanced=False)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
+    assert not np.isnan(got).any()
+    assert np.abs(got - ref).max() <= 2e-2
+    # request 4 claims 80 new tokens but holds 70: NaN rows for it only
+    m = np.array([257, 100, 96, 33, 80])
+    q, qs, got = run(w, dev, m, balanced=False)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=[0, 1, 2, 3])
+    assert np.isnan(got[qs[4]:qs[5]]).all()
+    assert np.abs(got[: qs[4]] - ref[: qs[4]]).max() <= 2e-2
+    # a launch sized for 200 new tokens: request 0 (257) is all NaN
+    m = np.array([257, 100, 96, 33, 64])
+    q, qs, got = run(w, dev, m, max_q=200, balanced=False)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=[1, 2, 3, 4])
+    assert np.isnan(got[qs[0]:qs[1]]).all()
+    assert np.abs(got[qs[1]:] - ref[qs[1]:]).max() <= 2e-2
+    # a bad table entry at request 3's key block 2: every workgroup of request 3
+    # reads it (all start at key 0), so all its rows are NaN; the others are right
+    tb = dev.block_tables.clone()
+    tb[3, 2] = -5
+    q, qs, got = run(w, dev, m, tables=tb, balanced=False)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale, rows=[0, 1, 2, 4])
+    assert np.isnan(got[qs[3]:qs[4]]).all()
+    keep = np.r_[qs[0]:qs[3], qs[4]:qs[5]]
+    assert np.abs(got[keep] - ref[keep]).max() <= 2e-2
 
 
 def test_balanced_verify_error_rows_and_workspace_reuse():
