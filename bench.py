@@ -237,7 +237,8 @@ def prefill_main(args, w):
     wsb = pa.prefill_workspace_bytes(w.batch, T, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
                                      dev.max_blocks, maxq)
     ws = pa.new_workspace(wsb) if wsb else None  # the faster paths' workspace, made once
-    path = pa.prefill_path(w.batch, w.num_q_heads, w.num_kv_heads, maxq, wsb)
+    path = pa.prefill_path(w.batch, w.num_q_heads, w.num_kv_heads, maxq, wsb, bf16=w.dtype == "bf16",
+                           head_dim=w.head_dim, block_size=w.block_size)
     log(f"pa_prefill path: {path}")
 
     def call():

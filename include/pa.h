@@ -190,9 +190,10 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  *   workspace    may be NULL: then a kernel with one wave per (kv-head,
  *                tile of query tokens, request) walks all of each tile's
  *                keys; for bfloat16 chunks of max_query_len * (num_q_heads /
- *                num_kv_heads) >= 128 columns, workgroups of four such tiles
- *                walk them together, each key/value step read from the pool
- *                once and shared through LDS.  The same holds with a
+ *                num_kv_heads) >= 128 columns (block size 16 or 32, or head
+ *                dim 64), workgroups of four such tiles walk them together,
+ *                each key/value step read from the pool once and shared
+ *                through LDS.  The same holds with a
  *                workspace when neither path below applies (see
  *                pa_prefill_workspace_bytes).  A caller that passes a workspace (256-byte aligned)
  *                of at least pa_prefill_workspace_bytes() bytes, when that is

@@ -324,15 +324,18 @@ def prefill_workspace_bytes(num_seqs: int, num_query_tokens: int, num_q_heads: i
 
 # bfloat16 chunks of at least this many (token, head) columns run on
 # workgroups of four query tiles sharing each key/value step through LDS
+# (except blocks of 8 with head dim 128)
 PREFILL_WORKGROUP_COLUMNS = 128
 
 
 def prefill_path(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_query_len: int, workspace_bytes: int,
-                 bf16: bool = True) -> str:
+                 bf16: bool = True, head_dim: int = 128, block_size: int = 16) -> str:
     """Which path pa_prefill takes given a workspace of ``workspace_bytes``
     sized by prefill_workspace_bytes (a description for logs)."""
     if not workspace_bytes:
-        if bf16 and max_query_len * (num_q_heads // num_kv_heads) >= PREFILL_WORKGROUP_COLUMNS:
+        # (blocks of 8 with head dim 128 keep the query tiles)
+        if (bf16 and not (head_dim == 128 and block_size == 8)
+                and max_query_len * (num_q_heads // num_kv_heads) >= PREFILL_WORKGROUP_COLUMNS):
             return "workgroup tiles"
         return "query tiles"
     if max_query_len * (num_q_heads // num_kv_heads) <= 16 and num_seqs <= 1024:

@@ -34,8 +34,12 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     return u >> 16;
 }
 
+// Two floats -> two bfloat16 in one word (lo in the low half), round to
+// nearest even: gfx950's packed conversion instruction (a NaN stays a NaN).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }

@@ -280,35 +280,50 @@ struct FlashEnt {
     int32_t e[NLD];
 };
 
-// Operands of one step (tokens tok0 .. tok0 + 31, clamped to last) from an
-// LDS slot holding the step's tiles; the same placement as issue_step_e.
+// LDS byte offsets (within a slot's key or value region) of a lane's
+// operands, the same for every step: step token s of the slot is token
+// s % BS of the slot's tile s / BS, and the placement is issue_step_e's.
+// No token is clamped: every slot is written in full, every read stays in
+// its slot, and tokens past the keys are masked by the step compute (scores
+// -inf, values zeroed bitwise).
 template <int D, int BS, int TSTRIDE>
-__device__ __forceinline__ void flash_read_step(StepRegs<true, D, BS>& r, const char* sk, const char* sv, int tok0,
-                                                int last, int n, int j) {
+struct FlashOffsets {
+    using C = DecodeCfg<true, D, BS>;
+    int k[C::NT];  // key tile t: + (4 c) BS 16 for chunk group c
+    int va, vb;    // values: + d BS 2 for head-dim row d (vb: second 8-byte half, blocks of 8)
+    __device__ void init(int n, int j) {
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t) {
+            const int srow = C::VIL ? 16 * (n >> 3) + 8 * t + (n & 7) : 16 * t + n;
+            k[t] = (srow / BS) * TSTRIDE + (srow % BS) * 16 + j * BS * 16;
+        }
+        if constexpr (C::VIL) {
+            va = (8 * j / BS) * TSTRIDE + (8 * j % BS) * 2 + n * BS * 2;
+            vb = 0;
+        } else {
+            va = (4 * j / BS) * TSTRIDE + (4 * j % BS) * 2 + n * BS * 2;
+            vb = ((16 + 4 * j) / BS) * TSTRIDE + ((16 + 4 * j) % BS) * 2 + n * BS * 2;
+        }
+    }
+};
+
+template <int D, int BS, int TSTRIDE>
+__device__ __forceinline__ void flash_read_step(StepRegs<true, D, BS>& r, const char* sk, const char* sv,
+                                                const FlashOffsets<D, BS, TSTRIDE>& o) {
     using C = DecodeCfg<true, D, BS>;
 #pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-        const int srow = C::VIL ? 16 * (n >> 3) + 8 * t + (n & 7) : 16 * t + n;
-        const int tok = min(tok0 + srow, last);
-        const char* kp = sk + (tok / BS - tok0 / BS) * TSTRIDE + (tok % BS) * 16;
+    for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-        for (int c = 0; c < C::NKC; ++c) r.k[t][c] = *reinterpret_cast<const u32x4*>(kp + (4 * c + j) * BS * 16);
-    }
+        for (int c = 0; c < C::NKC; ++c)
+            r.k[t][c] = *reinterpret_cast<const u32x4*>(sk + o.k[t] + 4 * c * BS * 16);
     if constexpr (C::VIL) {
-        const int tv = (tok0 + 16 * (j >> 1) <= last) ? tok0 + 8 * j : (last & ~7);
-        const char* vp = sv + (tv / BS - tok0 / BS) * TSTRIDE + (tv % BS) * 2;
 #pragma unroll
-        for (int c = 0; c < C::NV; ++c) r.v[c] = *reinterpret_cast<const u32x4*>(vp + (16 * c + n) * BS * 2);
+        for (int c = 0; c < C::NV; ++c) r.v[c] = *reinterpret_cast<const u32x4*>(sv + o.va + 16 * c * BS * 2);
     } else {
-        const int ta = min(tok0 + 4 * j, last & ~3);
-        const int tb = min(tok0 + 16 + 4 * j, last & ~3);
-        const char* va = sv + (ta / BS - tok0 / BS) * TSTRIDE + (ta % BS) * 2;
-        const char* vb = sv + (tb / BS - tok0 / BS) * TSTRIDE + (tb % BS) * 2;
 #pragma unroll
         for (int c = 0; c < C::NV; ++c) {
-            const int d = 16 * c + n;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(va + d * BS * 2);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vb + d * BS * 2);
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(sv + o.va + 16 * c * BS * 2);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(sv + o.vb + 16 * c * BS * 2);
             r.v[c] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
     }
@@ -324,7 +339,8 @@ struct FlashWave {
     const char* kbase;
     const char* vbase;
     const int32_t* trow;
-    int64_t blk_bytes;
+    uint32_t blk_bytes;  // bytes of one block (all kv-heads) in a pool
+    FlashOffsets<D, BS, F::TSTRIDE> off;
     int num_blocks, lastb, nst, kend, w, lane, n, j;
     float sl2;
     bool bad;
@@ -344,9 +360,9 @@ struct FlashWave {
             const int32_t e = E.e[i];
             const bool ok = e >= 0 && e < num_blocks;
             bad |= !ok;
-            const int64_t off = (int64_t)(ok ? e : 0) * blk_bytes + F::inner(w, i) + 16 * lane;
-            R.k[i] = ld16(kbase + off);
-            R.v[i] = ld16(vbase + off);
+            const uint64_t o = (uint64_t)(uint32_t)(ok ? e : 0) * blk_bytes + (uint32_t)(F::inner(w, i) + 16 * lane);
+            R.k[i] = ld16(kbase + o);
+            R.v[i] = ld16(vbase + o);
         }
     }
     __device__ __forceinline__ void put(const Stage& R, int slot) {
@@ -361,7 +377,7 @@ struct FlashWave {
     __device__ __forceinline__ void compute(int x, int slot) {
         StepRegs<true, D, BS> cur;
         const char* sk = lds + slot * 2 * F::SLOT;
-        flash_read_step<D, BS, F::TSTRIDE>(cur, sk, sk + F::SLOT, 32 * x, kend - 1, n, j);
+        flash_read_step<D, BS, F::TSTRIDE>(cur, sk, sk + F::SLOT, off);
 #pragma unroll
         for (int t = 0; t < NCT; ++t)
             compute_step<true, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, 32 * x, kend, j, sl2, Lcol[t],
@@ -426,7 +442,8 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
     W.lane = tid & 63;
     W.n = W.lane & 15;
     W.j = W.lane >> 4;
-    W.blk_bytes = (int64_t)Hkv * C::TILE * C::ES;
+    W.blk_bytes = (uint32_t)Hkv * C::TILE * C::ES;
+    W.off.init(W.n, W.j);
     W.kbase = reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES;
     W.vbase = reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES;
     W.trow = tables + (int64_t)b * max_blocks;
@@ -606,10 +623,16 @@ hipError_t launch_flash(const PrefillLaunch& a) {
     return hipGetLastError();
 }
 
+// Blocks of 8 with head dim 128 do not fit two waves per SIMD without
+// spilling inside the step loop; that shape keeps the query-tile kernel.
+inline bool flash_fits(int D, int BS) { return !(D == 128 && BS == 8); }
+
 template <int D>
 hipError_t flash_bs(int BS, const PrefillLaunch& a) {
     switch (BS) {
-        case 8: return launch_flash<D, 8>(a);
+        case 8:
+            if constexpr (D != 128) return launch_flash<D, 8>(a);
+            return hipErrorInvalidValue;  // not reached: flash_fits
         case 16: return launch_flash<D, 16>(a);
         default: return launch_flash<D, 32>(a);
     }
@@ -719,7 +742,7 @@ extern "C" pa_status pa_prefill(const void* q, const void* k_cache, const void* 
     if ((int64_t)a.n_tiles * a.ks.P > 65535) return PA_ERR_UNSUPPORTED;
     const int cols = qt_used * G;
     hipError_t e;
-    if (dtype == PA_BF16 && a.ks.PS == 0 &&
+    if (dtype == PA_BF16 && a.ks.PS == 0 && flash_fits(head_dim, block_size) &&
         (int64_t)max_query_len * G >= (int64_t)kFlashCols * flash_waves(head_dim)) {
         // chunks that fill a workgroup's tiles: workgroup tiles sharing each step through LDS
         e = head_dim == 128 ? flash_bs<128>(block_size, a) : flash_bs<64>(block_size, a);

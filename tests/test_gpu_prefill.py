@@ -112,7 +112,8 @@ def test_prefill_matches_oracle(case):
         ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
         assert not np.isnan(got).any()
         err = float(np.abs(got - ref).max())
-        path = pa.prefill_path(w.batch, hq, hkv, int(m.max()), wsb if bal else 0, bf16=dtype == "bf16")
+        path = pa.prefill_path(w.batch, hq, hkv, int(m.max()), wsb if bal else 0, bf16=dtype == "bf16",
+                               head_dim=d, block_size=bs)
         say(label, path, f"max abs err {err:.3e}")
         assert err <= TOL[dtype], (path, err)
 
@@ -167,7 +168,7 @@ def test_empty_chunks_and_error_rows_without_fault():
     assert np.abs(got[: qs[3]] - ref[: qs[3]]).max() <= 2e-2
 
 
-@pytest.mark.parametrize("bs,hq,d", [(8, 32, 128), (16, 64, 128), (32, 16, 64)])
+@pytest.mark.parametrize("bs,hq,d", [(8, 32, 64), (16, 64, 128), (32, 16, 64), (32, 32, 128)])
 def test_workgroup_tiles_error_rows_without_fault(bs, hq, d):
     """Chunks long enough for the workgroup path: odd and even step counts,
     waves past a request's tokens, then the error rows (too many new tokens,
@@ -180,7 +181,7 @@ def test_workgroup_tiles_error_rows_without_fault(bs, hq, d):
     dev = build_device_batch(w)
     dev.cache_append()
     m = np.array([257, 100, 96, 33, 64])
-    assert pa.prefill_path(w.batch, hq, hkv, int(m.max()), 0) == "workgroup tiles"
+    assert pa.prefill_path(w.batch, hq, hkv, int(m.max()), 0, head_dim=d, block_size=bs) == "workgroup tiles"
     say("workgroup tiles", "bs", bs, "G", g, "D", d, "M", list(m))
     q, qs, got = run(w, dev, m, balanced=False)
     ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
