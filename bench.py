@@ -4,8 +4,12 @@
                     [--partition-size P] [--no-cpu]
 
 One step is one pass of the whole hot path over one batch: the cache append
-of every sequence's decode token (pa_cache_write) followed by the decode
-attention (pa_decode, with its split-sequence merge when partitioned).  The
+of every sequence's decode token and the decode attention.  With the
+balanced split (the default for the Llama-3-8B and 70B shapes) both run in
+one launch (pa_decode_append: the launch stores the new tokens and attends
+to them from their input rows); otherwise, or with --step separate, the
+step is pa_cache_write followed by pa_decode (with its split-sequence merge
+when partitioned).  The
 inputs (pool, block tables, queries, decode tokens) are resident in HBM
 before the timed region starts.  The default workload is the
 Llama-3-8B-shaped decode layer: 64 sequences, 32 query / 8 KV heads, head
@@ -67,14 +71,14 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload: str, mode: str = "split"):
+def measured_traffic(workload: str, mode: str = "split", fused: bool = False):
     """HBM bytes per decode launch from the committed counter summary of this
     workload (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by their
     calibrations), or None when there is none or the decode sources changed
     since it was taken."""
     import hashlib
 
-    kernel = "pa_decode_shared_prefix" if mode == "shared" else "pa_decode"
+    kernel = "pa_decode_shared_prefix" if mode == "shared" else ("pa_decode_append" if fused else "pa_decode")
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
@@ -307,7 +311,8 @@ def shared_read_bytes(w, plan) -> int:
     return (own + once) * per_tok
 
 
-def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str, cold_iters: int = 20):
+def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str, cold_iters: int = 20,
+              fused: bool = False):
     import torch
 
     from paged_kv_cache_348_amd.workload import build_device_batch
@@ -326,11 +331,14 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str,
         log(f"shared-prefix plan: {plan.num_groups} groups, up to {plan.max_group} requests, "
             f"up to {plan.max_prefix_blocks} shared blocks")
         attend = lambda: dev.attend_shared(plan, partition_size=partition_size)  # noqa: E731
+    elif fused:
+        attend = dev.append_and_attend  # the append runs in the same launch
     else:
         attend = dev.attend
 
     def step():
-        dev.cache_append()
+        if not fused:
+            dev.cache_append()
         attend()
 
     for _ in range(warmup):
@@ -384,6 +392,8 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str,
     import paged_kv_cache_348_amd as pa
 
     read_bytes = shared_read_bytes(w, plan) if plan is not None else w.kv_read_bytes()
+    per_tok = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    algo_bytes = read_bytes + (int((w.seq_lens >= 1).sum()) * per_tok if fused else 0)  # + the stored new tokens
     nbytes = (read_bytes + 4095) // 4096 * 4096
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -438,7 +448,7 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str,
     return dict(ms_step=ms_step, wall_s=t_wall, hot_ms=hot, cold_ms=cold, ms_append=ms_append, out=out,
                 stream_read_gbps=nbytes / (sr_ms * 1e-3) / 1e9,
                 device=dev_name, width=dev.max_blocks, launches=dev.launches,
-                read_bytes=read_bytes, swap_ms=swap, swap_bytes=swap_bytes, swap_blocks=nsw)
+                read_bytes=read_bytes, algo_bytes=algo_bytes, swap_ms=swap, swap_bytes=swap_bytes, swap_blocks=nsw)
 
 
 def main(argv=None):
@@ -451,6 +461,9 @@ def main(argv=None):
     ap.add_argument("--decode", choices=("split", "shared"), default=None,
                     help="split: pa_decode; shared: pa_decode_shared_prefix (reads blocks shared by forked "
                          "requests once per group); default: shared for prefix_share, else split")
+    ap.add_argument("--step", choices=("fused", "separate"), default=None,
+                    help="fused: cache append and decode in one launch (pa_decode_append, balanced split only); "
+                         "separate: pa_cache_write then the decode; default: fused with the balanced split")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--block-order", choices=("seeded", "identity"), default="seeded",
@@ -481,6 +494,10 @@ def main(argv=None):
         ps = w.partition_size or DEFAULT_PARTITION.get(args.workload, 0)
     if mode == "shared" and ps <= 0:
         ps = 512
+    fused = (args.step or ("fused" if ps == PARTITION_BALANCED and mode == "split" else "separate")) == "fused"
+    if fused and (ps != PARTITION_BALANCED or mode != "split"):
+        print("--step fused runs on the balanced split (pa_decode_append)", file=sys.stderr)
+        return 2
     kv_bytes = w.kv_read_bytes()
     log(f"workload {w.name}: B {w.batch}, sum L {int(w.seq_lens.sum())}, KV bytes {kv_bytes / 1e9:.3f} GB, "
         f"partition {ps}, decode {mode}")
@@ -490,12 +507,13 @@ def main(argv=None):
         cpu, ref = cpu_baseline(w, min_seconds=args.cpu_seconds)
         log(f"cpu oracle: {cpu['value']:.1f} tok/s on {cpu['cores']} cores")
 
-    g = gpu_bench(w, args.steps, args.warmup, ps, mode)
+    g = gpu_bench(w, args.steps, args.warmup, ps, mode, fused=fused)
     ms = g["ms_step"]
     hot, cold = g["hot_ms"], g["cold_ms"]
     t_dec = float(np.median(hot)) * 1e-3
     read_bytes = g["read_bytes"]  # what the decode must read: logical KV bytes, or unique ones when shared
-    achieved = read_bytes / t_dec / 1e9
+    algo_bytes = g["algo_bytes"]  # + the new tokens' stores when the append runs in the same launch
+    achieved = algo_bytes / t_dec / 1e9
     err = None
     if ref is not None:
         err = float(np.abs(g["out"] - ref).max())
@@ -526,8 +544,9 @@ def main(argv=None):
             "block_size": w.block_size,
             "num_blocks": w.num_blocks,
             "partition_size": ps,
-            "step": "pa_cache_write (decode tokens) + "
-                    + ("pa_decode_shared_prefix" if mode == "shared" else "pa_decode"),
+            "step": ("pa_decode_append (the decode tokens' cache append and the decode in one launch)" if fused
+                     else "pa_cache_write (decode tokens) + "
+                     + ("pa_decode_shared_prefix" if mode == "shared" else "pa_decode")),
             "decode": mode,
             "block_order": args.block_order,
         },
@@ -548,15 +567,15 @@ def main(argv=None):
         "kv_tokens_per_s": float(w.seq_lens.sum()) / t_dec,
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode_shared_prefix" if mode == "shared" else "pa_decode",
+            "kernel": "pa_decode_shared_prefix" if mode == "shared" else ("pa_decode_append" if fused else "pa_decode"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": (measured_traffic(args.workload, mode)
+            "traffic": (measured_traffic(args.workload, mode, fused)
                         if ps == DEFAULT_PARTITION.get(args.workload, ps)
                         and mode == DEFAULT_DECODE.get(args.workload, "split") else None),
-            "algorithmic_bytes_per_launch": read_bytes,
+            "algorithmic_bytes_per_launch": algo_bytes,
             "flop_per_launch": flop,
         },
         "cpu_baseline": cpu,

@@ -170,6 +170,42 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
+ * One decode step in one launch: the cache append of each sequence's new
+ * token (pa_cache_write with one token per sequence) and pa_decode on the
+ * balanced split, with the same results.  The cache grows by the token a
+ * step adds and attention reads the table, pos / block_size and
+ * pos % block_size ("Paged attention in LLMs", "The cache being stored";
+ * MCQ page, code sketch); the launch attends to position L_b - 1 from the
+ * new token's row below instead of from its slot, so it never waits for
+ * its own stores.
+ *
+ *   k, v          device, [num_seqs][num_kv_heads][head_dim], dtype: row b
+ *                 is sequence b's token at position L_b - 1 (rows of
+ *                 sequences with L_b <= 0 are not read)
+ *   slot_mapping  device, int64 [num_seqs]: where row b is stored (slot =
+ *                 block * block_size + offset, as for pa_cache_write);
+ *                 outside [0, num_blocks * block_size) skips the store.  It
+ *                 should be position L_b - 1's slot in b's table: the result
+ *                 uses row b for that position whatever is stored there.
+ *   k_cache, v_cache  written (the new tokens) and read (positions
+ *                 0 .. L_b - 2)
+ *   workspace     as pa_decode with partition_size PA_PARTITION_BALANCED
+ *                 (pa_decode_workspace_bytes(..., PA_PARTITION_BALANCED),
+ *                 counters zero-filled once, left zero)
+ * Everything else as pa_decode; the same error rows (zeros for L_b <= 0,
+ * NaN for a length the table cannot hold or a table entry outside the pool
+ * among positions 0 .. L_b - 2); num_seqs <= 1024.  The stores of a call
+ * and any read of the same slots by another call must be ordered by the
+ * stream.
+ * ------------------------------------------------------------------------ */
+pa_status pa_decode_append(const void* q, const void* k, const void* v, const int64_t* slot_mapping,
+                           void* k_cache, void* v_cache, const int32_t* block_tables,
+                           const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out,
+                           void* stream, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           pa_dtype dtype, void* workspace, size_t workspace_bytes);
+
+/* ------------------------------------------------------------------------
  * Multi-token query over the paged cache: prefill, chunked prefill and
  * speculative verification.  Request b has L_b = seq_lens[b] tokens in the
  * cache, the last M_b of them new (their keys and values already written

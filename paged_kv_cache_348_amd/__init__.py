@@ -31,7 +31,7 @@ __all__ = [
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
     "new_workspace", "SharedPrefixPlan", "plan_shared_prefix", "decode_shared_prefix",
     "decode_shared_prefix_workspace_bytes", "shared_prefix_max_group", "simulate_memory", "PA_MEM_CONTIGUOUS",
-    "PA_MEM_PAGED", "swap_blocks", "prefill", "prefill_workspace_bytes", "prefill_path",
+    "PA_MEM_PAGED", "swap_blocks", "decode_append", "prefill", "prefill_workspace_bytes", "prefill_path",
 ]
 
 
@@ -194,6 +194,46 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale
                           _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), hkv, float(scale),
                           _dev(out, "out"), _stream_ptr(stream), B, hq, d, bs, nb, mb, _dtype_code(q.dtype),
                           partition_size, ws_ptr, ws_bytes), "pa_decode")
+    return out
+
+
+def decode_append(q, k, v, slot_mapping, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale: float,
+                  out=None, workspace=None, stream=None):
+    """One decode step in one launch (pa_decode_append): stores k[b], v[b]
+    ([B, Hkv, D], sequence b's token at position seq_lens[b] - 1) in slot
+    slot_mapping[b] (int64 [B]; out of range skips) and returns the decode
+    attention over positions 0 .. seq_lens[b] - 1, reading that position from
+    k[b], v[b].  Balanced split; ``workspace`` as for decode()."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    if hkv != num_kv_heads:
+        raise ValueError("num_kv_heads does not match the cache")
+    B, hq, dq = q.shape
+    if dq != d or q.dtype != k_cache.dtype:
+        raise ValueError("q must be [B, Hq, head_dim] in the cache dtype")
+    if tuple(k.shape) != (B, hkv, d) or k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B, num_kv_heads, head_dim] in the cache dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != B:
+        raise ValueError("slot_mapping must be int64 [B]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("seq_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if B == 0:
+        return out
+    mb = block_tables.shape[1]
+    need = decode_workspace_bytes(B, hq, hkv, d, bs, mb, PA_PARTITION_BALANCED)
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    check(lib().pa_decode_append(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"),
+                                 _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                                 _dev(seq_lens, "seq_lens"), hkv, float(scale), _dev(out, "out"), _stream_ptr(stream),
+                                 B, hq, d, bs, nb, mb, _dtype_code(q.dtype), _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size()), "pa_decode_append")
     return out
 
 

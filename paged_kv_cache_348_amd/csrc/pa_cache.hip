@@ -40,22 +40,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict
     const u32x4 vv = ld16(v + src);
     const int64_t s = slots[t];
     if (s < 0 || s >= total_slots) return;
-    const int64_t blk = s / BS;
-    const int off = (int)(s % BS);
-    const int64_t tile = (blk * Hkv + h) * (int64_t)D * BS;  // element offset of the (block, head) tile
-    st16(kc + (tile + ((int64_t)c * BS + off) * X) * ES, kv);
-    if constexpr (ES == 2) {
-        // bf16 blocks of 16 or 32 tokens store values with bits 2 and 3 of the
-        // in-block offset swapped (include/pa.h)
-        const int vpos = BS >= 16 ? (off & ~12) | ((off & 4) << 1) | ((off & 8) >> 1) : off;
-        uint16_t* vt = reinterpret_cast<uint16_t*>(vc) + tile + (int64_t)c * X * BS + vpos;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vt[(int64_t)e * BS] = (uint16_t)(vv[e >> 1] >> (16 * (e & 1)));
-    } else {
-        uint32_t* vt = reinterpret_cast<uint32_t*>(vc) + tile + (int64_t)c * X * BS + off;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vt[(int64_t)e * BS] = vv[e];
-    }
+    store_token_chunk<ES>(kc, vc, s, h, c, Hkv, D, BS, kv, vv);
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc,

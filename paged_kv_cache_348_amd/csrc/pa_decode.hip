@@ -429,14 +429,28 @@ __device__ __forceinline__ void finish_piece(const RunState<BF16, D, BS>& St, co
     first_piece = false;
 }
 
+// The decode step's new tokens for the fused append (pa_decode_append):
+// row b of k / v ([B][Hkv][D]) is sequence b's token at position L_b - 1,
+// stored to slot slots[b] (skipped outside [0, total_slots)) by the launch
+// that attends over it.
+struct AppendArgs {
+    const char* k;
+    const char* v;
+    const int64_t* slots;
+    char* kc;
+    char* vc;
+    int64_t total_slots;
+};
+
 // One wave's state in the balanced kernel and its pipeline stages.  For
 // compute step x an iteration (1) issues the key/value/query loads of step
 // x+1 with the table entries fetched one iteration earlier, (2) fetches the
 // entries of step x+2 with scalar loads and (3) computes step x.  A piece
 // ends where its segment ends or at the wave's last step.
-template <bool BF16, int D, int BS, bool MULTI>
+template <bool BF16, int D, int BS, bool MULTI, bool APPEND>
 struct BalancedWave {
     using C = DecodeCfg<BF16, D, BS>;
+    AppendArgs ap;  // APPEND: the new tokens
     const int32_t* s_qs;  // multi-token query: query_start in LDS
     int qi, qh;           // multi-token query: this lane's column as (token n / G, head n % G)
     const void* q_;
@@ -482,7 +496,15 @@ struct BalancedWave {
     }
 
     __device__ __forceinline__ void compute(StepRegs<BF16, D, BS>& buf, const typename C::QRegs& q) {
-        if constexpr (MULTI) {
+        if constexpr (APPEND) {
+            // the cache holds positions 0 .. L - 2; position L - 1 (not read
+            // from the cache, which this launch is writing) is added after the
+            // segment's last step.  A step with no cached position (the one
+            // step of a length-1 sequence, or a last step starting at L - 1)
+            // is skipped: a piece starting there keeps m = -inf, l = 0, acc = 0.
+            if (cc.ls * C::STEP < cc.L - 1)
+                compute_step<BF16, D, BS>(buf, q, St.m, St.l, St.acc, cc.ls * C::STEP, cc.L - 1, j, scale_log2);
+        } else if constexpr (MULTI) {
             // column n is query token n / G at position L - M + n / G: it sees keys up to there
             const int lim = cc.L - cc.M + 1;
             compute_step<BF16, D, BS, true>(buf, q, St.m, St.l, St.acc, cc.ls * C::STEP, cc.L, j, scale_log2,
@@ -493,6 +515,66 @@ struct BalancedWave {
         St.bad |= bad_c;
     }
 
+    // The new token's key chunks (4c + j) and value rows (16c + 4j ..) of
+    // segment (b, g) for this lane.  Loaded before the next step's loads, so
+    // waiting for them leaves those in flight.
+    struct NewRow {
+        u32x4 k[C::NKC];
+        u32x4 v[C::NV];  // bf16: the low half of each holds the lane's 4 values
+    };
+    __device__ __forceinline__ void load_new(NewRow& r) {
+        const int64_t row = ((int64_t)cc.b * Hkv + cc.g) * D * C::ES;
+#pragma unroll
+        for (int c = 0; c < C::NKC; ++c) r.k[c] = ld16(ap.k + row + (int64_t)(4 * c + j) * 16);
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) {
+            const int d0 = 16 * c + 4 * j;
+            if constexpr (BF16) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(ap.v + row + (int64_t)d0 * 2);
+                r.v[c] = u32x4{w[0], w[1], 0u, 0u};
+            } else {
+                r.v[c] = ld16(ap.v + row + (int64_t)d0 * 4);
+            }
+        }
+    }
+
+    // Position L - 1 of segment (b, g) from the new tokens' rows: its score
+    // for each head column (lane group j holds chunks 4c + j of the query
+    // and of the key), then one online-softmax update with its value row.
+    __device__ __forceinline__ void add_new(const typename C::QRegs& q, const NewRow& nr) {
+        float part = 0.0f;
+#pragma unroll
+        for (int c = 0; c < C::NKC; ++c) {
+            const u32x4 kv = nr.k[c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (BF16) {  // two bfloat16 per word, widened exactly
+                    part = fmaf(__uint_as_float(q[c][e] << 16), __uint_as_float(kv[e] << 16), part);
+                    part = fmaf(__uint_as_float(q[c][e] & 0xffff0000u), __uint_as_float(kv[e] & 0xffff0000u), part);
+                } else {
+                    part = fmaf(__uint_as_float(q[c][e]), __uint_as_float(kv[e]), part);
+                }
+            }
+        }
+        const float sc = wave_sum16(part) * scale_log2;
+        const float m_new = fmaxf(St.m, sc);
+        const float alpha = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(St.m - m_new);
+        const float p = __builtin_amdgcn_exp2f(sc - m_new);
+        St.l = St.l * alpha + p;
+        St.m = m_new;
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) {  // the lane's accumulator rows 16c + 4j ..
+            const u32x4 w = nr.v[c];
+            f32x4 vf;
+            if constexpr (BF16)
+                vf = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                           __uint_as_float(w[1] & 0xffff0000u)};
+            else
+                vf = __builtin_bit_cast(f32x4, w);
+            St.acc[c] = St.acc[c] * alpha + p * vf;
+        }
+    }
+
     __device__ __forceinline__ void finish() {
         finish_piece<BF16, D, BS, MULTI>(St, cc, seg_begin, first_piece, cut0, cut1, s_first, slot_o, slot_ml, out_, w, Hq,
                                   G, n, j);
@@ -501,6 +583,10 @@ struct BalancedWave {
     // one iteration for compute step x (x + 1 < wend): load into (bl, ql), compute (bc, qc)
     __device__ __forceinline__ void iter(StepRegs<BF16, D, BS>& bl, typename C::QRegs& ql,
                                          StepRegs<BF16, D, BS>& bc, const typename C::QRegs& qc, int64_t x) {
+        const bool seg_end = cc.ls == cc.nst - 1;
+        NewRow nr;
+        if constexpr (APPEND)
+            if (seg_end) load_new(nr);
         issue(bl, ql, ci, fe);
         bad_i = fe.bad;
         StepCursor cf = ci;
@@ -511,7 +597,10 @@ struct BalancedWave {
         // keep the compiler from hoisting the compute (and its wait) above the loads
         __builtin_amdgcn_sched_barrier(0);
         compute(bc, qc);
-        if (cc.ls == cc.nst - 1) finish();
+        if (seg_end) {
+            if constexpr (APPEND) add_new(qc, nr);
+            finish();
+        }
         cc = ci;
         bad_c = bad_i;
         ci = cf;
@@ -523,10 +612,35 @@ struct BalancedWave {
 
     // the wave's last step
     __device__ __forceinline__ void last(StepRegs<BF16, D, BS>& bc, const typename C::QRegs& qc) {
-        compute(bc, qc);
+        if constexpr (APPEND) {
+            NewRow nr;
+            const bool seg_end = cc.ls == cc.nst - 1;
+            if (seg_end) load_new(nr);
+            compute(bc, qc);
+            if (seg_end) add_new(qc, nr);
+        } else {
+            compute(bc, qc);
+        }
         finish();
     }
 };
+
+// The fused append's stores: wave w stores (sequence, kv-head) rows w,
+// w + grid, ... of the new tokens (lane c: 16-byte chunk c of the key and of
+// the value) in the layout pa_cache_write uses.  Nothing in the launch reads
+// those slots, so a wave issues them after its own work and never waits for
+// them (partial-line value stores are slow to complete).
+template <int ES, int D, int BS>
+__device__ __forceinline__ void append_rows(const AppendArgs& ap, int w, int rows, int Hkv, int lane) {
+    constexpr int NCH = D * ES / 16;  // 16-byte chunks of a key row
+    for (int r = w; r < rows; r += gridDim.x) {
+        const int64_t sl = ap.slots[r / Hkv];
+        if (lane < NCH && sl >= 0 && sl < ap.total_slots) {
+            const int64_t src = (int64_t)r * D * ES + (int64_t)lane * 16;
+            store_token_chunk<ES>(ap.kc, ap.vc, sl, r % Hkv, lane, Hkv, D, BS, ld16(ap.k + src), ld16(ap.v + src));
+        }
+    }
+}
 
 // Balanced split ("stream-K" over the attention's token steps).
 //
@@ -546,13 +660,18 @@ struct BalancedWave {
 // MULTI: a multi-token query (query_start given): segment (b, g) has the
 // M_b * G columns (token, head) of sequence b's M_b new tokens, M_b * G <= 16,
 // each masked causally at its own position.
-template <bool BF16, int D, int BS, bool MULTI>
+// APPEND (decode only): the launch also stores the decode step's new tokens
+// (ap) in their slots and attends to position L_b - 1 from ap's rows, so it
+// never reads the slots it writes.
+template <bool BF16, int D, int BS, bool MULTI, bool APPEND = false>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(
     const void* __restrict__ q_, const void* __restrict__ kc_, const void* __restrict__ vc_,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens, void* __restrict__ out_,
     float* __restrict__ slot_o, float* __restrict__ slot_ml, int32_t* __restrict__ counters, int B, int Hq,
-    int Hkv, int G, int max_blocks, int num_blocks, float scale_log2, const int32_t* __restrict__ q_start, int T) {
+    int Hkv, int G, int max_blocks, int num_blocks, float scale_log2, const int32_t* __restrict__ q_start, int T,
+    AppendArgs ap) {
     using C = DecodeCfg<BF16, D, BS>;
+    static_assert(!(MULTI && APPEND), "the fused append is a decode");
     __shared__ int64_t s_first[kBalancedMaxSeqs];  // global step where sequence b's segments start
     __shared__ int32_t s_steps[kBalancedMaxSeqs];  // steps per segment of sequence b (0: no work)
     __shared__ int32_t s_len[kBalancedMaxSeqs];    // length of sequence b
@@ -619,7 +738,10 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
         }
     }
     const int nw = (int)min((int64_t)gridDim.x, S);
-    if (w >= nw) return;
+    if (w >= nw) {
+        if constexpr (APPEND) append_rows<C::ES, D, BS>(ap, w, B * Hkv, Hkv, lane);
+        return;
+    }
     const int64_t wbeg = S * w / nw;
     const int64_t wend = S * (w + 1) / nw;
 
@@ -648,7 +770,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
 
     // 4. the pipeline: stage buffers A and B alternate, so no loaded
     //    register is ever copied (a copy would have to wait for its load)
-    BalancedWave<BF16, D, BS, MULTI> W;
+    BalancedWave<BF16, D, BS, MULTI, APPEND> W;
+    W.ap = ap;
     W.s_qs = s_qs;
     W.qi = MULTI ? n / G : 0;
     W.qh = MULTI ? n % G : 0;
@@ -704,6 +827,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
         if (cut1.valid)
             count_in<BF16, D, BS, MULTI>(cut1, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
     }
+    // 6. the new tokens' stores, last: nothing in the launch waits for them
+    if constexpr (APPEND) append_rows<C::ES, D, BS>(ap, w, B * Hkv, Hkv, lane);
 }
 
 }  // namespace pa
@@ -765,6 +890,8 @@ struct Launch {
     int T;
     float sl2;
     hipStream_t stream;
+    bool append;  // the fused append (balanced split): ap holds the new tokens
+    pa::AppendArgs ap;
 };
 
 template <bool BF16, int D, int BS>
@@ -774,11 +901,17 @@ hipError_t launch_decode(const Launch& a) {
         if (a.q_start)
             hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, true>), dim3((unsigned)balanced_waves()),
                                dim3(64), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
-                               a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, a.q_start, a.T);
+                               a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, a.q_start, a.T,
+                               pa::AppendArgs{});
+        else if (a.append)
+            hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, false, true>), dim3((unsigned)balanced_waves()),
+                               dim3(64), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
+                               a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, nullptr, 0, a.ap);
         else
             hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, false>), dim3((unsigned)balanced_waves()),
                                dim3(64), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
-                               a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, nullptr, 0);
+                               a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, nullptr, 0,
+                               pa::AppendArgs{});
         return hipGetLastError();
     }
     dim3 grid((unsigned)a.Hkv, (unsigned)a.P_max, (unsigned)a.B);
@@ -820,12 +953,12 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
     return cnt + align_up(rows * head_dim * sizeof(float)) + align_up(rows * 2 * sizeof(float));
 }
 
-extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, const int32_t* seq_lens, int32_t num_kv_heads,
-                               float scale, void* out, void* stream, int32_t num_seqs, int32_t num_q_heads,
-                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                               int32_t max_blocks_per_seq, pa_dtype dtype, int32_t partition_size,
-                               void* workspace, size_t workspace_bytes) {
+// pa_decode, and with `ap` the fused append (pa_decode_append) on the balanced split.
+static pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                             const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out, void* stream,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_blocks_per_seq, pa_dtype dtype, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, const pa::AppendArgs* ap) {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
         partition_size < PA_PARTITION_BALANCED || !std::isfinite(scale))
         return PA_ERR_INVALID_ARG;
@@ -845,6 +978,9 @@ extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v
     if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return PA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+        return PA_ERR_INVALID_ARG;
+    if (ap && (!ap->k || !ap->v || !ap->slots || !aligned16(ap->k) || !aligned16(ap->v) ||
+               (reinterpret_cast<uintptr_t>(ap->slots) & 7u)))
         return PA_ERR_INVALID_ARG;
 
     int64_t ps = 0, pmax = 1;
@@ -882,12 +1018,40 @@ extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v
     a.balanced = balanced;
     a.sl2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
     a.stream = reinterpret_cast<hipStream_t>(stream);
+    a.append = ap != nullptr;
+    if (ap) a.ap = *ap;
     hipError_t e;
     if (dtype == PA_BF16)
         e = head_dim == 128 ? dispatch_bs<true, 128>(block_size, a) : dispatch_bs<true, 64>(block_size, a);
     else
         e = head_dim == 128 ? dispatch_bs<false, 128>(block_size, a) : dispatch_bs<false, 64>(block_size, a);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+extern "C" pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens, int32_t num_kv_heads,
+                               float scale, void* out, void* stream, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, pa_dtype dtype, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes) {
+    return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, stream, num_seqs,
+                       num_q_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, dtype, partition_size,
+                       workspace, workspace_bytes, nullptr);
+}
+
+extern "C" pa_status pa_decode_append(const void* q, const void* k, const void* v, const int64_t* slot_mapping,
+                                      void* k_cache, void* v_cache, const int32_t* block_tables,
+                                      const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out,
+                                      void* stream, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                      pa_dtype dtype, void* workspace, size_t workspace_bytes) {
+    if (num_blocks < 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
+    pa::AppendArgs ap{reinterpret_cast<const char*>(k), reinterpret_cast<const char*>(v), slot_mapping,
+                      reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache),
+                      (int64_t)num_blocks * block_size};
+    return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, stream, num_seqs,
+                       num_q_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, dtype,
+                       PA_PARTITION_BALANCED, workspace, workspace_bytes, &ap);
 }
 
 // ---- multi-token query on the balanced split (pa_prefill's path for

@@ -44,6 +44,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Store 16-byte chunk c (head-dim elements c*X .. c*X + X - 1, X = 16 / ES)
+// of one token's key (kv) and value (vv) for kv-head h into slot s of a pool
+// of blocks of BS tokens, in the pool's tile layout: keys [D/X][BS][X],
+// values [D][BS] per (block, head), bf16 values in blocks of 16 or 32 at the
+// in-block offset with bits 2 and 3 swapped.  One key store, X value stores.
+template <int ES>
+__device__ __forceinline__ void store_token_chunk(char* __restrict__ kc, char* __restrict__ vc, int64_t s, int h,
+                                                  int c, int Hkv, int D, int BS, u32x4 kv, u32x4 vv) {
+    constexpr int X = 16 / ES;
+    const int64_t blk = s / BS;
+    const int off = (int)(s % BS);
+    const int64_t tile = (blk * Hkv + h) * (int64_t)D * BS;  // element offset of the (block, head) tile
+    st16(kc + (tile + ((int64_t)c * BS + off) * X) * ES, kv);
+    if constexpr (ES == 2) {
+        const int vpos = BS >= 16 ? (off & ~12) | ((off & 4) << 1) | ((off & 8) >> 1) : off;
+        uint16_t* vt = reinterpret_cast<uint16_t*>(vc) + tile + (int64_t)c * X * BS + vpos;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vt[(int64_t)e * BS] = (uint16_t)(vv[e >> 1] >> (16 * (e & 1)));
+    } else {
+        uint32_t* vt = reinterpret_cast<uint32_t*>(vc) + tile + (int64_t)c * X * BS + off;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vt[(int64_t)e * BS] = vv[e];
+    }
+}
+
 // Wave-uniform copy of a lane's value (v_readlane_b32).
 __device__ __forceinline__ int32_t lane_value(int32_t v, int lane) {
     return __builtin_amdgcn_readlane(v, lane);

@@ -16,8 +16,9 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-from . import (Allocator, cache_write, copy_blocks, decode, decode_shared_prefix, decode_shared_prefix_workspace_bytes,
-               decode_workspace_bytes, new_kv_cache, new_workspace, plan_shared_prefix, shared_prefix_max_group)
+from . import (PA_PARTITION_BALANCED, Allocator, cache_write, copy_blocks, decode, decode_append, decode_shared_prefix,
+               decode_shared_prefix_workspace_bytes, decode_workspace_bytes, new_kv_cache, new_workspace,
+               plan_shared_prefix, shared_prefix_max_group)
 
 
 def _torch():
@@ -55,6 +56,14 @@ class DeviceBatch:
     host_dec_slots: np.ndarray
     launches: dict = field(default_factory=dict)
     shared_workspace: Optional[object] = None
+    # the decode step's new tokens per sequence for the fused append
+    # (pa_decode_append): row b is position L_b - 1, stored at new_slots[b]
+    # (-1: a sequence without a decode-step token, its last position already
+    # in the cache, or L_b = 0)
+    new_k: Optional[object] = None
+    new_v: Optional[object] = None
+    new_slots: Optional[object] = None
+    fused_workspace: Optional[object] = None
 
     @property
     def max_blocks(self) -> int:
@@ -62,6 +71,17 @@ class DeviceBatch:
 
     def cache_append(self, stream=None) -> None:
         cache_write(self.dec_k, self.dec_v, self.dec_slots, self.k_cache, self.v_cache, stream=stream)
+
+    def append_and_attend(self, stream=None, out=None):
+        """The cache append and the decode in one launch (pa_decode_append)."""
+        w = self.workload
+        if self.fused_workspace is None:
+            self.fused_workspace = new_workspace(
+                decode_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                       self.max_blocks, PA_PARTITION_BALANCED), self.q.device)
+        return decode_append(self.q, self.new_k, self.new_v, self.new_slots, self.k_cache, self.v_cache,
+                             self.block_tables, self.seq_lens, w.num_kv_heads, w.scale,
+                             out=self.out if out is None else out, workspace=self.fused_workspace, stream=stream)
 
     def attend(self, stream=None, partition_size: Optional[int] = None, out=None):
         w = self.workload
@@ -214,6 +234,16 @@ def build_device_batch(w, device="cuda", partition_size: Optional[int] = None, n
         dk.append(k)
         dv.append(v)
     shape = (0, w.num_kv_heads, w.head_dim)
+    # per-sequence rows for the fused append: position L - 1 of every sequence
+    nk = np.zeros((w.batch, w.num_kv_heads, w.head_dim), w.np_dtype)
+    nv = np.zeros_like(nk)
+    nslots = np.full(w.batch, -1, dtype=np.int64)
+    for i, b in enumerate(rows):
+        nk[b], nv[b], nslots[b] = dk[i][0], dv[i][0], dslots[i]
+    for b, s in enumerate(w.seq_ids):
+        if s not in dec and lens[b] >= 1:
+            k, v = w.token_kv(s, int(lens[b]) - 1, 1)
+            nk[b], nv[b] = k[0], v[0]
     dk = np.concatenate(dk) if dk else np.empty(shape, w.np_dtype)
     dv = np.concatenate(dv) if dv else np.empty(shape, w.np_dtype)
 
@@ -228,4 +258,6 @@ def build_device_batch(w, device="cuda", partition_size: Optional[int] = None, n
         dec_k=to_device(dk, w.dtype, device), dec_v=to_device(dv, w.dtype, device),
         dec_slots=torch.from_numpy(dslots).to(device), out=torch.empty_like(q), workspace=ws,
         partition_size=ps, host_tables=tables, host_lens=lens, host_dec_slots=dslots, launches=bat.launches,
+        new_k=to_device(nk, w.dtype, device), new_v=to_device(nv, w.dtype, device),
+        new_slots=torch.from_numpy(nslots).to(device),
     )
