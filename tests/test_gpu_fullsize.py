@@ -100,3 +100,33 @@ def test_full_size_shared_prefix_sampled_rows():
         say("prefix_share shared row", b, "L", int(w.seq_lens[b]), "max abs err", f"{err:.3e}")
         assert err <= TOL, (b, err)
     w.drop_kv()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,nsample", [("llama3_8b", 6), ("llama_70b", 4)])
+def test_full_size_one_launch_step_sampled_rows(name, nsample):
+    """The decode step as the benchmark times it on the balanced split: the
+    append and the decode in one launch (pa_decode_append), on a pool that
+    does not yet hold the step's tokens."""
+    w = make_workload(name, seed=0)
+    say(name, "one launch: B", w.batch, "sum L", int(w.seq_lens.sum()))
+    dev = build_device_batch(w, partition_size=BAL)
+    out = dev.append_and_attend()
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite output"
+    rng = np.random.default_rng(4321)
+    rows = sorted({int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))}
+                  | set(int(x) for x in rng.choice(w.batch, size=nsample, replace=False)))
+    for b in rows:
+        K, V = w.sequence_kv(b)
+        ref = oa.dense_attention(oa.widen(w.q[b]), oa.widen(K), oa.widen(V), w.scale)
+        err = float(np.abs(got[b] - ref).max())
+        say(name, "one launch row", b, "L", int(w.seq_lens[b]), "max abs err", f"{err:.3e}")
+        assert err <= TOL, (name, b, err)
+        blk, off = divmod(int(dev.host_dec_slots[b]), w.block_size)
+        key = dev.k_cache[blk, :, :, off, :].reshape(w.num_kv_heads, w.head_dim)
+        val = dev.v_cache[blk, :, :, pa.value_position(off, w.block_size, dev.v_cache.dtype)]
+        assert np.array_equal(bits(key), K[-1]), "decode-token key not stored in its slot"
+        assert np.array_equal(bits(val), V[-1]), "decode-token value not stored in its slot"
+    w.drop_kv()
