@@ -115,6 +115,39 @@ def test_decode_rejects_bad_arguments(kw, expect):
     assert decode_call(**kw) == expect
 
 
+def decode_append_call(**kw):
+    a = dict(q=fake(), k=fake(), v=fake(), slots=fake(), kc=fake(), vc=fake(), bt=fake(), sl=fake(), hkv=8,
+             scale=0.1, out=fake(), stream=None, B=4, hq=32, d=128, bs=16, nb=100, mb=8, dt=1,
+             ws=fake(0x20000), wsb=1 << 30)
+    a.update(kw)
+    return _l().pa_decode_append(a["q"], a["k"], a["v"], a["slots"], a["kc"], a["vc"], a["bt"], a["sl"], a["hkv"],
+                                 a["scale"], a["out"], a["stream"], a["B"], a["hq"], a["d"], a["bs"], a["nb"],
+                                 a["mb"], a["dt"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=None), pa.PA_ERR_INVALID_ARG),                 # the new tokens are required
+    (dict(v=None), pa.PA_ERR_INVALID_ARG),
+    (dict(slots=None), pa.PA_ERR_INVALID_ARG),
+    (dict(k=fake(0x10008)), pa.PA_ERR_INVALID_ARG),        # rows must be 16-byte aligned
+    (dict(slots=fake(0x10004)), pa.PA_ERR_INVALID_ARG),    # int64 slots
+    (dict(ws=None), pa.PA_ERR_INVALID_ARG),                # the balanced split's workspace
+    (dict(wsb=16), pa.PA_ERR_INVALID_ARG),
+    (dict(B=1025), pa.PA_ERR_UNSUPPORTED),                 # too many sequences to balance
+    (dict(hq=30), pa.PA_ERR_INVALID_ARG),
+    (dict(d=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=24), pa.PA_ERR_UNSUPPORTED),
+    (dict(dt=5), pa.PA_ERR_UNSUPPORTED),
+    (dict(nb=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), pa.PA_ERR_INVALID_ARG),
+    (dict(B=0, q=None, k=None, v=None, slots=None, kc=None, vc=None, bt=None, sl=None, out=None, ws=None),
+     pa.PA_OK),
+])
+def test_decode_append_rejects_bad_arguments(kw, expect):
+    """The one-launch decode step validates everything on the host, before any launch."""
+    assert decode_append_call(**kw) == expect
+
+
 def test_workspace_size_formula():
     # partitions of 512 over 8 blocks of 16 = 128 tokens: one partition, no workspace
     assert pa.decode_workspace_bytes(4, 32, 8, 128, 16, 8, 512) == 0
