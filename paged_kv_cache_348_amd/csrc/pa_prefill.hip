@@ -239,19 +239,21 @@ __global__ __launch_bounds__(1024) void prefill_merge_kernel(const float* __rest
 
 // ---------------------------------------------------------------------------- workgroup tiles (bfloat16)
 //
-// Long chunks.  A workgroup of NW waves takes NW consecutive wave tiles of query tokens of one (kv-head, request) — each
-// wave NCT 16-column matrix-core tiles of (token, head) columns, as in
-// prefill_kernel — and walks the keys once for all of them, up to its last
-// token's position.  Every 32-token step of keys and values is copied from
-// the pool into a two-slot LDS ring by all the workgroup's lanes: a lane's
-// 16-byte pieces of a step are loaded two steps ahead into registers (the
+// Long chunks.  A workgroup of NW waves takes NW consecutive wave tiles of
+// query tokens of one (kv-head, request): each wave holds NCT 16-column
+// matrix-core tiles of (token, head) columns, as in prefill_kernel, and the
+// workgroup walks the keys once for all of them, up to its last token's
+// position.  Every 32-token step of keys and values is copied from the pool
+// into a two-slot LDS ring by all the workgroup's lanes: a lane's 16-byte
+// pieces of a step are loaded two steps ahead into registers (the
 // block-table entries they need one load earlier still, so waiting for an
-// entry never waits for the step just issued), and written to the ring one
+// entry never waits for the step just issued) and written to the ring one
 // step ahead; the waves read their operands from the ring in the order
 // prefill_kernel reads them from the pool.  One barrier per step separates
 // the writes into a slot from the reads of the step before.  A step's keys
 // and values are read from the pool once per workgroup instead of once per
-// wave.
+// wave, and two waves fit a SIMD (at most 256 registers each), so one
+// wave's softmax work overlaps the other's matrix-core work.
 
 template <int D, int BS, int NW>
 struct FlashCfg {
@@ -603,17 +605,16 @@ hipError_t launch_prefill(const PrefillLaunch& a) {
 
 // Workgroup tiles for bfloat16 chunks (prefill_flash_kernel): kFlashCols
 // columns per wave, two waves per SIMD (the register budget that allows),
-// flash_waves<D>() waves per workgroup.
+// kFlashWaves waves per workgroup.  Measured on MI355X (512 new tokens per
+// request, Llama-3-8B shape): 64 columns at one wave per SIMD and eight
+// waves per workgroup were both slower.
 constexpr int kFlashCols = 32;
 constexpr int kFlashWavesPerSimd = 2;
-constexpr int kFlashWavesD128 = 4;
-template <int D>
-constexpr int flash_waves() { return D == 128 ? kFlashWavesD128 : 4; }
-inline int flash_waves(int D) { return D == 128 ? flash_waves<128>() : flash_waves<64>(); }
+constexpr int kFlashWaves = 4;
 
 template <int D, int BS>
 hipError_t launch_flash(const PrefillLaunch& a) {
-    constexpr int NW = flash_waves<D>();
+    constexpr int NW = kFlashWaves;
     const int QTw = kFlashCols / a.G;
     const int QTW = QTw * NW;
     hipLaunchKernelGGL((pa::prefill_flash_kernel<D, BS, NW, kFlashCols / 16, kFlashWavesPerSimd>),
@@ -743,7 +744,7 @@ extern "C" pa_status pa_prefill(const void* q, const void* k_cache, const void* 
     const int cols = qt_used * G;
     hipError_t e;
     if (dtype == PA_BF16 && a.ks.PS == 0 && flash_fits(head_dim, block_size) &&
-        (int64_t)max_query_len * G >= (int64_t)kFlashCols * flash_waves(head_dim)) {
+        (int64_t)max_query_len * G >= (int64_t)kFlashCols * kFlashWaves) {
         // chunks that fill a workgroup's tiles: workgroup tiles sharing each step through LDS
         e = head_dim == 128 ? flash_bs<128>(block_size, a) : flash_bs<64>(block_size, a);
         return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
