@@ -440,7 +440,7 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
 
     W_t W;
     W.lds = lds;
-    W.w = tid >> 6;
+    W.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: entry loads and piece bases go scalar
     W.lane = tid & 63;
     W.n = W.lane & 15;
     W.j = W.lane >> 4;
