@@ -362,9 +362,11 @@ struct FlashWave {
             const int32_t e = E.e[i];
             const bool ok = e >= 0 && e < num_blocks;
             bad |= !ok;
-            const uint64_t o = (uint64_t)(uint32_t)(ok ? e : 0) * blk_bytes + (uint32_t)(F::inner(w, i) + 16 * lane);
-            R.k[i] = ld16(kbase + o);
-            R.v[i] = ld16(vbase + o);
+            // the piece's base is wave-uniform (scalar registers); the lane's
+            // 16 bytes are added last, as the load's vector offset
+            const uint64_t o = (uint64_t)(uint32_t)(ok ? e : 0) * blk_bytes + (uint32_t)F::inner(w, i);
+            R.k[i] = ld16(kbase + o + 16 * lane);
+            R.v[i] = ld16(vbase + o + 16 * lane);
         }
     }
     __device__ __forceinline__ void put(const Stage& R, int slot) {
