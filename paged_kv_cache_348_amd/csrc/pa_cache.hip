@@ -20,7 +20,7 @@
 
 namespace pa {
 
-template <int ES>
+template <int ES, bool NT>
 __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict__ k, const char* __restrict__ v,
                                                           const int64_t* __restrict__ slots, char* __restrict__ kc,
                                                           char* __restrict__ vc, int64_t n_chunks, int Hkv, int D,
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict
     const u32x4 vv = ld16(v + src);
     const int64_t s = slots[t];
     if (s < 0 || s >= total_slots) return;
-    store_token_chunk<ES>(kc, vc, s, h, c, Hkv, D, BS, kv, vv);
+    store_token_chunk<ES, NT>(kc, vc, s, h, c, Hkv, D, BS, kv, vv);
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc,
@@ -86,6 +86,10 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(const char* __restrict
 namespace {
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// pa_cache_write launches of up to this many tokens (a decode step's batch)
+// store non-temporally; larger ones (prefill appends) through write-back.
+constexpr int32_t kNonTemporalMaxTokens = 4096;
+
 // Address a kernel can use for p: device memory as is, pinned host memory
 // (hipHostMalloc) through its device mapping; anything else (pageable host
 // memory, unknown pointers) gives nullptr.
@@ -126,16 +130,28 @@ extern "C" pa_status pa_cache_write(const void* k, const void* v, const int64_t*
     if (grid > 2147483647LL) return PA_ERR_UNSUPPORTED;
     const int64_t total_slots = (int64_t)num_blocks * block_size;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (dtype == PA_BF16)
-        hipLaunchKernelGGL((pa::cache_write_kernel<2>), dim3((unsigned)grid), dim3(256), 0, s,
-                           reinterpret_cast<const char*>(k), reinterpret_cast<const char*>(v), slot_mapping,
-                           reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache), chunks, num_kv_heads,
-                           head_dim, block_size, total_slots);
-    else
-        hipLaunchKernelGGL((pa::cache_write_kernel<4>), dim3((unsigned)grid), dim3(256), 0, s,
-                           reinterpret_cast<const char*>(k), reinterpret_cast<const char*>(v), slot_mapping,
-                           reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache), chunks, num_kv_heads,
-                           head_dim, block_size, total_slots);
+    const char* kp = reinterpret_cast<const char*>(k);
+    const char* vp = reinterpret_cast<const char*>(v);
+    char* kcp = reinterpret_cast<char*>(k_cache);
+    char* vcp = reinterpret_cast<char*>(v_cache);
+    // decode-sized appends (about one token per block) store non-temporally,
+    // bulk appends through write-back (see store_token_chunk)
+    const bool nt = num_tokens <= kNonTemporalMaxTokens;
+    if (dtype == PA_BF16) {
+        if (nt)
+            hipLaunchKernelGGL((pa::cache_write_kernel<2, true>), dim3((unsigned)grid), dim3(256), 0, s, kp, vp,
+                               slot_mapping, kcp, vcp, chunks, num_kv_heads, head_dim, block_size, total_slots);
+        else
+            hipLaunchKernelGGL((pa::cache_write_kernel<2, false>), dim3((unsigned)grid), dim3(256), 0, s, kp, vp,
+                               slot_mapping, kcp, vcp, chunks, num_kv_heads, head_dim, block_size, total_slots);
+    } else {
+        if (nt)
+            hipLaunchKernelGGL((pa::cache_write_kernel<4, true>), dim3((unsigned)grid), dim3(256), 0, s, kp, vp,
+                               slot_mapping, kcp, vcp, chunks, num_kv_heads, head_dim, block_size, total_slots);
+        else
+            hipLaunchKernelGGL((pa::cache_write_kernel<4, false>), dim3((unsigned)grid), dim3(256), 0, s, kp, vp,
+                               slot_mapping, kcp, vcp, chunks, num_kv_heads, head_dim, block_size, total_slots);
+    }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -637,7 +637,8 @@ __device__ __forceinline__ void append_rows(const AppendArgs& ap, int w, int row
         const int64_t sl = ap.slots[r / Hkv];
         if (lane < NCH && sl >= 0 && sl < ap.total_slots) {
             const int64_t src = (int64_t)r * D * ES + (int64_t)lane * 16;
-            store_token_chunk<ES>(ap.kc, ap.vc, sl, r % Hkv, lane, Hkv, D, BS, ld16(ap.k + src), ld16(ap.v + src));
+            store_token_chunk<ES, true>(ap.kc, ap.vc, sl, r % Hkv, lane, Hkv, D, BS, ld16(ap.k + src),
+                                        ld16(ap.v + src));
         }
     }
 }

@@ -48,29 +48,46 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_x
 // of one token's key (kv) and value (vv) for kv-head h into slot s of a pool
 // of blocks of BS tokens, in the pool's tile layout: keys [D/X][BS][X],
 // values [D][BS] per (block, head), bf16 values in blocks of 16 or 32 at the
-// in-block offset with bits 2 and 3 swapped.  One key store, X value stores,
-// all non-temporal: a decode step's tokens are not read again by the launch
-// that writes them, and the scattered value stores (partial lines) leave
-// sooner than through write-back at the end of the kernel (measured: the
-// two-call decode step 104.2 -> 101.3 us, the one-launch step 99.6 -> 98.5 us).
-template <int ES>
+// in-block offset with bits 2 and 3 swapped.  One key store, X value stores.
+// NT: non-temporal stores, for launches that write one token per block (a
+// decode step): its scattered value stores are partial lines, which leave
+// sooner this way than through write-back at the end of the kernel
+// (measured: the two-call decode step 104.2 -> 101.3 us, the one-launch step
+// 99.6 -> 98.5 us).  Appends of many tokens per block keep write-back stores,
+// which L2 merges into whole lines (with NT a bulk append of 139k tokens took
+// 8.1 ms instead of 1.2 ms).
+template <int ES, bool NT>
 __device__ __forceinline__ void store_token_chunk(char* __restrict__ kc, char* __restrict__ vc, int64_t s, int h,
                                                   int c, int Hkv, int D, int BS, u32x4 kv, u32x4 vv) {
     constexpr int X = 16 / ES;
     const int64_t blk = s / BS;
     const int off = (int)(s % BS);
     const int64_t tile = (blk * Hkv + h) * (int64_t)D * BS;  // element offset of the (block, head) tile
-    __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(kc + (tile + ((int64_t)c * BS + off) * X) * ES));
+    u32x4* kp = reinterpret_cast<u32x4*>(kc + (tile + ((int64_t)c * BS + off) * X) * ES);
+    if constexpr (NT)
+        __builtin_nontemporal_store(kv, kp);
+    else
+        *kp = kv;
     if constexpr (ES == 2) {
         const int vpos = BS >= 16 ? (off & ~12) | ((off & 4) << 1) | ((off & 8) >> 1) : off;
         uint16_t* vt = reinterpret_cast<uint16_t*>(vc) + tile + (int64_t)c * X * BS + vpos;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            __builtin_nontemporal_store((uint16_t)(vv[e >> 1] >> (16 * (e & 1))), vt + (int64_t)e * BS);
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t x = (uint16_t)(vv[e >> 1] >> (16 * (e & 1)));
+            if constexpr (NT)
+                __builtin_nontemporal_store(x, vt + (int64_t)e * BS);
+            else
+                vt[(int64_t)e * BS] = x;
+        }
     } else {
         uint32_t* vt = reinterpret_cast<uint32_t*>(vc) + tile + (int64_t)c * X * BS + off;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) __builtin_nontemporal_store(vv[e], vt + (int64_t)e * BS);
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (NT)
+                __builtin_nontemporal_store(vv[e], vt + (int64_t)e * BS);
+            else
+                vt[(int64_t)e * BS] = vv[e];
+        }
     }
 }
 
