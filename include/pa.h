@@ -245,9 +245,10 @@ pa_status pa_decode_append(const void* q, const void* k, const void* v, const in
  *                  block_size spans two 2,048-token key partitions or more):
  *                  the tile kernel with its keys cut into partitions, whose
  *                  partial results a merge kernel combines (log-sum-exp
- *                  rule).  The workspace's first pa_decode_counter_bytes()
- *                  bytes are left untouched; the rest may hold anything on
- *                  entry.
+ *                  rule; a tile whose keys fit the first partition writes
+ *                  its rows directly).  The workspace's first
+ *                  pa_decode_counter_bytes() bytes are left untouched; the
+ *                  rest may hold anything on entry.
  *                A workspace smaller than required gives PA_ERR_INVALID_ARG.
  *                Calls sharing a workspace must not overlap.
  *   num_q_heads / num_kv_heads <= 16; the other arguments as for pa_decode.

@@ -627,9 +627,11 @@ struct BalancedWave {
 
 // The fused append's stores: wave w stores (sequence, kv-head) rows w,
 // w + grid, ... of the new tokens (lane c: 16-byte chunk c of the key and of
-// the value) in the layout pa_cache_write uses.  Nothing in the launch reads
-// those slots, so a wave issues them after its own work and never waits for
-// them (partial-line value stores are slow to complete).
+// the value) in the layout pa_cache_write uses, non-temporally.  Nothing in
+// the launch reads those slots, so a wave issues them after all its own
+// work and never waits for them: issued earlier, they would hold up the
+// wave's next load wait (loads and stores complete in issue order), and the
+// partial-line value stores are slow to complete.
 template <int ES, int D, int BS>
 __device__ __forceinline__ void append_rows(const AppendArgs& ap, int w, int rows, int Hkv, int lane) {
     constexpr int NCH = D * ES / 16;  // 16-byte chunks of a key row

@@ -150,7 +150,9 @@ __global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_
             compute_step<BF16, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, tok0, kend, j, scale_log2,
                                             Lcol[t], min(pos0 + (16 * t) / G + 1, kend));
     }
-    if (ks.PS == 0) {
+    if (ks.PS == 0 || Lend <= ks.PS) {
+        // no split, or the tile's keys fit partition 0 (p = 0 here): the rows
+        // themselves, which the merge leaves alone
 #pragma unroll
         for (int t = 0; t < NCT; ++t) {
             const int c = 16 * t + n;
@@ -184,7 +186,8 @@ __global__ __launch_bounds__(64) void prefill_kernel(const void* __restrict__ q_
 // The merge, on the tile kernel's grid (kv-head, query tile, request) with
 // 16 waves per workgroup, one query row per wave at a time: the same checks
 // as the tile kernel decide which tiles it wrote partials for (error rows are
-// its NaN rows, left alone here) and over how many partitions.
+// its NaN rows, and a tile whose keys fit one partition its finished rows,
+// both left alone here) and over how many partitions.
 template <bool BF16, int D>
 __global__ __launch_bounds__(1024) void prefill_merge_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
@@ -209,6 +212,7 @@ __global__ __launch_bounds__(1024) void prefill_merge_kernel(const float* __rest
     const int nq = min(QT, M - q0);
     const int Lend = L - M + q0 + nq;
     const int np = (Lend + PS - 1) / PS;  // partitions the tile's waves wrote
+    if (np < 2) return;
     for (int c = wv; c < nq * G; c += 16) {
         const int64_t row = (int64_t)(t0 + q0 + c / G) * Hq + g * G + c % G;
         const float* ml = part_ml + row * P * 2;
