@@ -229,11 +229,11 @@ pa_status pa_decode_append(const void* q, const void* k, const void* v, const in
  *                num_kv_heads) >= 128 columns (block size 16 or 32, or head
  *                dim 64), workgroups of four such tiles walk them together,
  *                each key/value step read from the pool once and shared
- *                through LDS.  The same holds with a
- *                workspace when neither path below applies (see
- *                pa_prefill_workspace_bytes).  A caller that passes a workspace (256-byte aligned)
- *                of at least pa_prefill_workspace_bytes() bytes, when that is
- *                not 0, gets one of two faster paths:
+ *                through LDS.  The same holds with a workspace when
+ *                neither path below applies (see pa_prefill_workspace_bytes).
+ *                A caller that passes a workspace (256-byte aligned) of at
+ *                least pa_prefill_workspace_bytes() bytes, when that is not
+ *                0, gets one of two faster paths:
  *                - verification-sized chunks (max_query_len * (num_q_heads /
  *                  num_kv_heads) <= 16, num_seqs <= 1024): pa_decode's
  *                  balanced split, each request's (token, head) pairs one
