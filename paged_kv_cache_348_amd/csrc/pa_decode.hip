@@ -199,6 +199,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 
 constexpr int kBalancedMaxSeqs = 1024;   // sequences a balanced call may hold
 constexpr int kBalancedMaxWaves = 2048;  // waves (and partial-slot pairs) of a balanced call
+constexpr int kBalancedWavesPerGroup = 2;  // waves of a balanced workgroup (independent, one LDS table each)
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
@@ -633,9 +634,10 @@ struct BalancedWave {
 // wave's next load wait (loads and stores complete in issue order), and the
 // partial-line value stores are slow to complete.
 template <int ES, int D, int BS>
-__device__ __forceinline__ void append_rows(const AppendArgs& ap, int w, int rows, int Hkv, int lane) {
+__device__ __forceinline__ void append_rows(const AppendArgs& ap, int w, int nwaves, int rows, int Hkv,
+                                            int lane) {
     constexpr int NCH = D * ES / 16;  // 16-byte chunks of a key row
-    for (int r = w; r < rows; r += gridDim.x) {
+    for (int r = w; r < rows; r += nwaves) {
         const int64_t sl = ap.slots[r / Hkv];
         if (lane < NCH && sl >= 0 && sl < ap.total_slots) {
             const int64_t src = (int64_t)r * D * ES + (int64_t)lane * 16;
@@ -667,7 +669,7 @@ __device__ __forceinline__ void append_rows(const AppendArgs& ap, int w, int row
 // (ap) in their slots and attends to position L_b - 1 from ap's rows, so it
 // never reads the slots it writes.
 template <bool BF16, int D, int BS, bool MULTI, bool APPEND = false>
-__global__ __launch_bounds__(64) void decode_balanced_kernel(
+__global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_balanced_kernel(
     const void* __restrict__ q_, const void* __restrict__ kc_, const void* __restrict__ vc_,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens, void* __restrict__ out_,
     float* __restrict__ slot_o, float* __restrict__ slot_ml, int32_t* __restrict__ counters, int B, int Hq,
@@ -675,14 +677,22 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     AppendArgs ap) {
     using C = DecodeCfg<BF16, D, BS>;
     static_assert(!(MULTI && APPEND), "the fused append is a decode");
-    __shared__ int64_t s_first[kBalancedMaxSeqs];  // global step where sequence b's segments start
-    __shared__ int32_t s_steps[kBalancedMaxSeqs];  // steps per segment of sequence b (0: no work)
-    __shared__ int32_t s_len[kBalancedMaxSeqs];    // length of sequence b
-    __shared__ int32_t s_qs[MULTI ? kBalancedMaxSeqs + 1 : 1];  // multi-token query: query_start
-    const int lane = threadIdx.x;
+    // each wave of the workgroup has its own copy of the tables
+    constexpr int WPG = kBalancedWavesPerGroup;
+    __shared__ int64_t s_first_g[WPG][kBalancedMaxSeqs];  // global step where sequence b's segments start
+    __shared__ int32_t s_steps_g[WPG][kBalancedMaxSeqs];  // steps per segment of sequence b (0: no work)
+    __shared__ int32_t s_len_g[WPG][kBalancedMaxSeqs];    // length of sequence b
+    __shared__ int32_t s_qs_g[WPG][MULTI ? kBalancedMaxSeqs + 1 : 1];  // multi-token query: query_start
+    const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t* s_first = s_first_g[sub];
+    int32_t* s_steps = s_steps_g[sub];
+    int32_t* s_len = s_len_g[sub];
+    int32_t* s_qs = s_qs_g[sub];
+    const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int j = lane >> 4;
-    const int w = blockIdx.x;
+    const int w = blockIdx.x * WPG + sub;  // this wave
+    const int nwaves = gridDim.x * WPG;
 
     // 1. step counts of every sequence and their prefix sums (each wave
     //    computes the same table; the length loads are issued together)
@@ -725,7 +735,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
 
     // 2. rows no segment covers: empty sequences (zeros) and lengths the
     //    table cannot hold (NaN)
-    for (int b = w; b < B; b += gridDim.x) {
+    for (int b = w; b < B; b += nwaves) {
         if (s_steps[b] == 0) {
             const int L = lens[b];
             if constexpr (MULTI) {
@@ -740,9 +750,9 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
             }
         }
     }
-    const int nw = (int)min((int64_t)gridDim.x, S);
+    const int nw = (int)min((int64_t)nwaves, S);
     if (w >= nw) {
-        if constexpr (APPEND) append_rows<C::ES, D, BS>(ap, w, B * Hkv, Hkv, lane);
+        if constexpr (APPEND) append_rows<C::ES, D, BS>(ap, w, nwaves, B * Hkv, Hkv, lane);
         return;
     }
     const int64_t wbeg = S * w / nw;
@@ -831,7 +841,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
             count_in<BF16, D, BS, MULTI>(cut1, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
     }
     // 6. the new tokens' stores, last: nothing in the launch waits for them
-    if constexpr (APPEND) append_rows<C::ES, D, BS>(ap, w, B * Hkv, Hkv, lane);
+    if constexpr (APPEND) append_rows<C::ES, D, BS>(ap, w, nwaves, B * Hkv, Hkv, lane);
 }
 
 }  // namespace pa
@@ -864,9 +874,12 @@ inline void partition_plan(int32_t block_size, int32_t max_blocks, int32_t parti
     }
 }
 
-// Waves of a balanced call: kWavesPerCU per compute unit of the current device.
-// Measured on MI355X (Llama-3-8B-shaped batch): 2 per CU reads fastest; 4
-// is ~3 % slower and more than 4 no longer fit in one round.
+// Waves of a balanced call: kWavesPerCU per compute unit of the current device,
+// launched kBalancedWavesPerGroup to a workgroup.  Measured on MI355X
+// (Llama-3-8B-shaped batch): 2 per CU reads fastest; 4 is ~3 % slower and
+// more than 4 no longer fit in one round.  Two waves per workgroup instead
+// of one ran 0.3-0.6 % faster in every paired run (the Llama-3-8B and
+// 70B shapes, with and without the fused append).
 constexpr int kWavesPerCU = 2;
 int balanced_waves() {
     static int cached[64] = {0};
@@ -876,7 +889,8 @@ int balanced_waves() {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        cached[dev] = std::min(pa::kBalancedMaxWaves, kWavesPerCU * cus);
+        cached[dev] = std::min(pa::kBalancedMaxWaves, kWavesPerCU * cus) / pa::kBalancedWavesPerGroup *
+                      pa::kBalancedWavesPerGroup;
     }
     return cached[dev];
 }
@@ -902,17 +916,17 @@ hipError_t launch_decode(const Launch& a) {
     const int G = a.Hq / a.Hkv;
     if (a.balanced) {
         if (a.q_start)
-            hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, true>), dim3((unsigned)balanced_waves()),
-                               dim3(64), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
+            hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, true>), dim3((unsigned)(balanced_waves() / pa::kBalancedWavesPerGroup)),
+                               dim3(64 * pa::kBalancedWavesPerGroup), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
                                a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, a.q_start, a.T,
                                pa::AppendArgs{});
         else if (a.append)
-            hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, false, true>), dim3((unsigned)balanced_waves()),
-                               dim3(64), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
+            hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, false, true>), dim3((unsigned)(balanced_waves() / pa::kBalancedWavesPerGroup)),
+                               dim3(64 * pa::kBalancedWavesPerGroup), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
                                a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, nullptr, 0, a.ap);
         else
-            hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, false>), dim3((unsigned)balanced_waves()),
-                               dim3(64), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
+            hipLaunchKernelGGL((pa::decode_balanced_kernel<BF16, D, BS, false>), dim3((unsigned)(balanced_waves() / pa::kBalancedWavesPerGroup)),
+                               dim3(64 * pa::kBalancedWavesPerGroup), 0, a.stream, a.q, a.kc, a.vc, a.tables, a.lens, a.out, a.po, a.pml,
                                a.counters, a.B, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.sl2, nullptr, 0,
                                pa::AppendArgs{});
         return hipGetLastError();
