@@ -99,6 +99,23 @@ def measured_traffic(workload: str, mode: str = "split", fused: bool = False):
 # ---------------------------------------------------------------------------- CPU baseline (the oracle)
 
 _CPU = {}
+# Worker processes of the oracle's pool at most: a one-GPU share of the host
+# (what the machine gives one GPU's jobs, whatever the affinity mask shows).
+CPU_POOL_CAP = 16
+
+
+def host_cores():
+    """(cores in this process's affinity, worker processes used)."""
+    affinity = len(os.sched_getaffinity(0))
+    return affinity, max(1, min(CPU_POOL_CAP, affinity))
+
+
+def close_pool(p):
+    """End a worker pool by letting its workers exit (close + join): a
+    terminate() would signal them, which a profiler attached to this
+    process reports as an abort."""
+    p.close()
+    p.join()
 
 
 def _cpu_init():
@@ -137,11 +154,12 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_passes: int = 10000):
     pool, _, tables, _, _ = replay(w)
     log(f"oracle replay {time.perf_counter() - t0:.1f}s")
     _CPU.update(k=pool.k, v=pool.v, tables=tables, lens=w.seq_lens, q=w.q, scale=w.scale)
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity, cores = host_cores()
     ctx = mp.get_context("fork")
     out = np.zeros((w.batch, w.num_q_heads, w.head_dim))
     order = sorted(range(w.batch), key=lambda b: -int(w.seq_lens[b]))  # longest first
-    with ctx.Pool(cores, initializer=_cpu_init) as p:
+    p = ctx.Pool(cores, initializer=_cpu_init)
+    try:
         passes = 0
         t0 = time.perf_counter()
         while True:
@@ -151,14 +169,18 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_passes: int = 10000):
             el = time.perf_counter() - t0
             if el >= min_seconds or passes >= max_passes:
                 break
+    finally:
+        close_pool(p)
     tok = passes * w.batch
     res = {
         "value": tok / el,
         "unit": "decode tokens/s",
         "cores": cores,
+        "affinity_cores": affinity,
         "kind": "oracle",
         "sample": f"the whole batch ({w.batch} sequences, sum L = {int(w.seq_lens.sum())}) x {passes} passes, "
-                  f"{el:.1f} s; float64 numpy, one sequence per task in a {cores}-process pool",
+                  f"{el:.1f} s; float64 numpy, one sequence per task in a {cores}-process pool "
+                  f"({affinity} cores in this process's affinity, capped at {CPU_POOL_CAP})",
         "kv_read_gbps": passes * w.kv_read_bytes() / el / 1e9,
     }
     _CPU.clear()
@@ -182,12 +204,13 @@ def cpu_prefill_baseline(w, q, qs, min_seconds: float = 10.0, max_passes: int = 
 
     pool, _, tables, _, _ = replay(w)
     _CPU.update(k=pool.k, v=pool.v, tables=tables, lens=w.seq_lens, q=q, qs=qs, scale=w.scale)
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity, cores = host_cores()
     ctx = mp.get_context("fork")
     order = sorted(range(w.batch), key=lambda b: -int(w.seq_lens[b]))
     out = np.zeros((int(qs[-1]), w.num_q_heads, w.head_dim))
     done_tok, done_req = 0, 0
-    with ctx.Pool(cores, initializer=_cpu_init) as p:
+    p = ctx.Pool(cores, initializer=_cpu_init)
+    try:
         t0 = time.perf_counter()
         for _ in range(max_passes):
             for b, o in p.imap_unordered(_cpu_prefill_one, order):
@@ -197,10 +220,14 @@ def cpu_prefill_baseline(w, q, qs, min_seconds: float = 10.0, max_passes: int = 
             el = time.perf_counter() - t0
             if el >= min_seconds:
                 break
+    finally:
+        close_pool(p)
     _CPU.clear()
-    return {"value": done_tok / el, "unit": "query tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": done_tok / el, "unit": "query tokens/s", "cores": cores, "affinity_cores": affinity,
+            "kind": "oracle",
             "sample": f"{done_req} requests ({done_tok} query tokens), {el:.1f} s; float64 numpy, one request per "
-                      f"task in a {cores}-process pool"}, out
+                      f"task in a {cores}-process pool ({affinity} cores in this process's affinity, capped at "
+                      f"{CPU_POOL_CAP})"}, out
 
 
 def prefill_flops(w, qs) -> float:
@@ -451,6 +478,38 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str,
                 read_bytes=read_bytes, algo_bytes=algo_bytes, swap_ms=swap, swap_bytes=swap_bytes, swap_blocks=nsw)
 
 
+def cold_only_main(args, w, ps, mode, fused):
+    """N decode launches of the step, each right after a 1 GiB read that
+    evicts L2 and MALL (a read leaves no dirty lines to write back during the
+    launch), with no events: under a kernel trace every launch of the decode
+    kernel is a cold one, timed without event overhead."""
+    import torch
+
+    from paged_kv_cache_348_amd.workload import build_device_batch
+
+    dev = build_device_batch(w, device="cuda", partition_size=ps)
+    w.drop_kv()
+    if mode == "shared":
+        plan = dev.shared_plan()
+        attend = lambda: dev.attend_shared(plan, partition_size=ps)  # noqa: E731
+    elif fused:
+        attend = dev.append_and_attend
+    else:
+        dev.cache_append()
+        attend = dev.attend
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.cold_only):
+        scratch.amax()
+        attend()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    print(json.dumps({"cold_only": args.cold_only, "workload": w.name, "partition_size": ps, "decode": mode,
+                      "fused": fused, "wall_s": el}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -470,6 +529,10 @@ def main(argv=None):
                     help="identity: the free pool starts in address order, so each sequence's blocks are "
                          "mostly adjacent (the block-table lookup-overhead comparison)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cold-only", type=int, default=0, metavar="N",
+                    help="run only N decode launches of the step, each after a 1 GiB read that evicts L2 and "
+                         "MALL, with no events around them (for a kernel trace of cold launches), then print "
+                         "one JSON line")
     ap.add_argument("--prefill", type=int, default=0,
                     help="measure pa_prefill instead: the last N tokens of each request are new queries "
                          "(causal multi-token query: speculative verification, chunked prefill)")
@@ -501,6 +564,8 @@ def main(argv=None):
     kv_bytes = w.kv_read_bytes()
     log(f"workload {w.name}: B {w.batch}, sum L {int(w.seq_lens.sum())}, KV bytes {kv_bytes / 1e9:.3f} GB, "
         f"partition {ps}, decode {mode}")
+    if args.cold_only:
+        return cold_only_main(args, w, ps, mode, fused)
 
     cpu, ref = (None, None)
     if not args.no_cpu:
@@ -513,7 +578,12 @@ def main(argv=None):
     t_dec = float(np.median(hot)) * 1e-3
     read_bytes = g["read_bytes"]  # what the decode must read: logical KV bytes, or unique ones when shared
     algo_bytes = g["algo_bytes"]  # + the new tokens' stores when the append runs in the same launch
-    achieved = algo_bytes / t_dec / 1e9
+    # the dominant kernel's launch time: with the one-launch step, the timed
+    # region's own average (one launch per step); otherwise the decode alone,
+    # back to back between one event pair (median of three runs)
+    t_launch = ms * 1e-3 if fused else t_dec
+    achieved = algo_bytes / t_launch / 1e9
+    t_cold = float(np.median(cold)) * 1e-3
     err = None
     if ref is not None:
         err = float(np.abs(g["out"] - ref).max())
@@ -572,6 +642,12 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
+            "timing": ("timed region: one launch per step" if fused else
+                       "decode alone, back-to-back launches between one event pair"),
+            # L2 and MALL evicted before each launch (a 1 GiB read), one event
+            # pair per launch, median of the launches
+            "achieved_cold": algo_bytes / t_cold / 1e9,
+            "frac_cold": algo_bytes / t_cold / 1e9 / HBM_PEAK_GBPS,
             "traffic": (measured_traffic(args.workload, mode, fused)
                         if ps == DEFAULT_PARTITION.get(args.workload, ps)
                         and mode == DEFAULT_DECODE.get(args.workload, "split") else None),

@@ -54,6 +54,18 @@ def _elem_bytes(dtype) -> int:
     return 2 if _dtype_code(dtype) == PA_BF16 else 4
 
 
+def _on_stream(stream):
+    """Context for the tensors a call makes itself (``out``, a zero-filled
+    workspace): they are allocated, and the workspace filled, on the launch
+    stream, so the launch follows the fill in stream order and the caching
+    allocator does not hand the memory to another stream while the launch
+    may still use it.  With no stream given the launch stream is the current
+    one and nothing changes."""
+    import contextlib
+
+    return contextlib.nullcontext() if stream is None else _torch().cuda.stream(stream)
+
+
 def _stream_ptr(stream) -> int:
     torch = _torch()
     if stream is None:
@@ -180,7 +192,8 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale
     if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
         raise ValueError("seq_lens must be int32 [B]")
     if out is None:
-        out = torch.empty_like(q)
+        with _on_stream(stream):
+            out = torch.empty_like(q)
     if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
         raise ValueError("out must match q")
     mb = block_tables.shape[1]
@@ -188,7 +201,8 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, scale
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
-            workspace = new_workspace(need, q.device)
+            with _on_stream(stream):
+                workspace = new_workspace(need, q.device)
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     check(lib().pa_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                           _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), hkv, float(scale),
@@ -220,7 +234,8 @@ def decode_append(q, k, v, slot_mapping, k_cache, v_cache, block_tables, seq_len
     if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
         raise ValueError("seq_lens must be int32 [B]")
     if out is None:
-        out = torch.empty_like(q)
+        with _on_stream(stream):
+            out = torch.empty_like(q)
     if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
         raise ValueError("out must match q")
     if B == 0:
@@ -228,7 +243,8 @@ def decode_append(q, k, v, slot_mapping, k_cache, v_cache, block_tables, seq_len
     mb = block_tables.shape[1]
     need = decode_workspace_bytes(B, hq, hkv, d, bs, mb, PA_PARTITION_BALANCED)
     if workspace is None:
-        workspace = new_workspace(need, q.device)
+        with _on_stream(stream):
+            workspace = new_workspace(need, q.device)
     check(lib().pa_decode_append(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"),
                                  _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
                                  _dev(seq_lens, "seq_lens"), hkv, float(scale), _dev(out, "out"), _stream_ptr(stream),
@@ -320,7 +336,8 @@ def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, num_kv_hea
     if plan.d_prefix_blocks.numel() != B:
         raise ValueError("plan was made for another batch")
     if out is None:
-        out = torch.empty_like(q)
+        with _on_stream(stream):
+            out = torch.empty_like(q)
     if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
         raise ValueError("out must match q")
     mb = block_tables.shape[1]
@@ -329,7 +346,8 @@ def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, num_kv_hea
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
-            workspace = new_workspace(need, q.device)
+            with _on_stream(stream):
+                workspace = new_workspace(need, q.device)
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     check(lib().pa_decode_shared_prefix(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
@@ -408,7 +426,8 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_hea
     if seq_lens.dtype != torch.int32 or query_start.dtype != torch.int32 or query_start.numel() != B + 1:
         raise ValueError("seq_lens must be int32 [B] and query_start int32 [B + 1]")
     if out is None:
-        out = torch.empty_like(q)
+        with _on_stream(stream):
+            out = torch.empty_like(q)
     if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
         raise ValueError("out must match q")
     if B == 0 or T == 0:
@@ -418,7 +437,8 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_hea
             if balanced else 0)
     if need:
         if workspace is None:
-            workspace = new_workspace(need, q.device)
+            with _on_stream(stream):
+                workspace = new_workspace(need, q.device)
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     check(lib().pa_prefill(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),

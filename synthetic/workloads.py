@@ -32,6 +32,10 @@ Workload shapes (the sizes of the five decode layers the path is measured on):
 * ``long_ctx_bs{8,16,32}``: 8 sequences, lengths uniform in [32768, 131072];
   32 query / 8 KV heads; head dim 128; bfloat16; split into 512-token
   partitions; the same lengths and values for each block size.
+
+The Llama-3-8B, 70B and long-context shapes also come in float32
+(``dtype="f32"``, names ending ``_f32``): the same lengths, placement and
+draws, left unrounded, for parity at the float32 tolerance at full size.
 """
 from __future__ import annotations
 
@@ -221,20 +225,24 @@ def tiny(seed: int = 0, **_):
     return _simple_batch("tiny", 0, seed, "f32", 8, 8, 64, 16, [14, 60, 1, 33], 64)
 
 
-def llama3_8b(seed: int = 0, batch: int = 64, len_lo: int = 512, len_hi: int = 4096, **_):
+def _named(base: str, dtype: str) -> str:
+    return base if dtype == "bf16" else f"{base}_{dtype}"
+
+
+def llama3_8b(seed: int = 0, batch: int = 64, len_lo: int = 512, len_hi: int = 4096, dtype: str = "bf16", **_):
     lens = _rng(seed, 1, S_LENS).integers(len_lo, len_hi + 1, size=batch)
-    return _simple_batch("llama3_8b", 1, seed, "bf16", 32, 8, 128, 16, lens, _pool_for(lens, 16))
+    return _simple_batch(_named("llama3_8b", dtype), 1, seed, dtype, 32, 8, 128, 16, lens, _pool_for(lens, 16))
 
 
 def long_ctx(seed: int = 0, block_size: int = 16, batch: int = 8, len_lo: int = 32768,
-             len_hi: int = 131072, partition_size: int = 512, **_):
+             len_hi: int = 131072, partition_size: int = 512, dtype: str = "bf16", **_):
     lens = _rng(seed, 4, S_LENS).integers(len_lo, len_hi + 1, size=batch)
-    w = _simple_batch(f"long_ctx_bs{block_size}", 4, seed, "bf16", 32, 8, 128, block_size, lens,
+    w = _simple_batch(_named(f"long_ctx_bs{block_size}", dtype), 4, seed, dtype, 32, 8, 128, block_size, lens,
                       _pool_for(lens, block_size), partition_size=partition_size)
     return w
 
 
-def llama_70b(seed: int = 0, batch: int = 256, len_lo: int = 1024, len_hi: int = 8192, **_):
+def llama_70b(seed: int = 0, batch: int = 256, len_lo: int = 1024, len_hi: int = 8192, dtype: str = "bf16", **_):
     """Interleaved arrival/finish trace that fragments the pool.
 
     2*batch requests draw target lengths; requests [0, batch) survive and are
@@ -281,11 +289,11 @@ def llama_70b(seed: int = 0, batch: int = 256, len_lo: int = 1024, len_hi: int =
     num_blocks = int(math.ceil(1.1 * max(peak1, peak3)))
     lens = targets[:batch].astype(np.int32)
     w = Workload(
-        name="llama_70b", config_id=cfg, seed=seed, dtype="bf16", num_q_heads=64, num_kv_heads=8,
+        name=_named("llama_70b", dtype), config_id=cfg, seed=seed, dtype=dtype, num_q_heads=64, num_kv_heads=8,
         head_dim=128, block_size=bs, num_blocks=num_blocks, scale=1.0 / math.sqrt(128),
         partition_size=0, seq_ids=list(range(batch)), seq_lens=lens,
         free_order=_rng(seed, cfg, S_FREE_ORDER).permutation(num_blocks).astype(np.int32),
-        ops=ops, q=_draw_q(seed, cfg, batch, 64, 128, "bf16"),
+        ops=ops, q=_draw_q(seed, cfg, batch, 64, 128, dtype),
     )
     w._runs = lambda seq, a, e: [(seq, a, e - a)]
     w._owner_len = {r: int(targets[r]) for r in range(batch)}
@@ -358,6 +366,12 @@ WORKLOADS = {
     "long_ctx_bs8": lambda seed=0, **kw: long_ctx(seed, block_size=8, **kw),
     "long_ctx_bs16": lambda seed=0, **kw: long_ctx(seed, block_size=16, **kw),
     "long_ctx_bs32": lambda seed=0, **kw: long_ctx(seed, block_size=32, **kw),
+    # the same shapes in float32
+    "llama3_8b_f32": lambda seed=0, **kw: llama3_8b(seed, dtype="f32", **kw),
+    "llama_70b_f32": lambda seed=0, **kw: llama_70b(seed, dtype="f32", **kw),
+    "long_ctx_bs8_f32": lambda seed=0, **kw: long_ctx(seed, block_size=8, dtype="f32", **kw),
+    "long_ctx_bs16_f32": lambda seed=0, **kw: long_ctx(seed, block_size=16, dtype="f32", **kw),
+    "long_ctx_bs32_f32": lambda seed=0, **kw: long_ctx(seed, block_size=32, dtype="f32", **kw),
 }
 
 

@@ -273,3 +273,28 @@ def test_balanced_split_many_sequences():
             if L == 0:
                 assert np.array_equal(out[b], np.zeros_like(out[b]))
         check_out(out, ref, w.dtype, what=f"many ps={ps}")
+
+
+def test_side_stream_calls_make_their_own_buffers_on_that_stream():
+    """A call given a stream other than the current one, without out or
+    workspace, allocates (and zero-fills) them on that stream, so the launch
+    follows the fill: every mode gives the current-stream result bit for bit."""
+    w = make_workload("llama3_8b", batch=6, len_lo=1, len_hi=700)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    args = (dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.seq_lens, w.num_kv_heads, w.scale)
+    for ps in (0, 64, BAL):
+        want = host_bits(pa.decode(*args, partition_size=ps))
+        side.wait_stream(torch.cuda.current_stream())
+        got = pa.decode(*args, partition_size=ps, stream=side)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(got), want), ps
+        say("side stream, partition", ps, "bit-identical")
+    want = host_bits(dev.append_and_attend())
+    side.wait_stream(torch.cuda.current_stream())
+    got = pa.decode_append(dev.q, dev.new_k, dev.new_v, dev.new_slots, dev.k_cache, dev.v_cache, dev.block_tables,
+                           dev.seq_lens, w.num_kv_heads, w.scale, stream=side)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(got), want)
