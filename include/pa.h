@@ -206,6 +206,38 @@ pa_status pa_decode_append(const void* q, const void* k, const void* v, const in
                            pa_dtype dtype, void* workspace, size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
+ * pa_decode_append without a workspace and without allocating: for callers
+ * that cannot allocate device memory (code under stream capture into a
+ * graph, serving loops that forbid allocation, harnesses that disallow it).
+ * Arguments, result, pool bytes and errors are those of pa_decode_append;
+ * the caller still passes every input and `out`.  The balanced split's
+ * merge counters and cut-piece partials live instead in a static device
+ * array of the library, 16 MiB, one per GPU the library runs on, held
+ * until the process ends.
+ *
+ * Limit: the scratch a call needs is 8 KiB of counters plus
+ * 2 * W * G * (head_dim + 2) * 4 bytes of partials (each 256-byte aligned),
+ * W = 2 * the device's compute units (512 on MI355X), G = num_q_heads /
+ * num_kv_heads; a shape needing more than 16 MiB returns
+ * PA_ERR_UNSUPPORTED with nothing enqueued (on MI355X every supported shape
+ * fits: G 16 with head_dim 128 needs about 8.2 MiB).
+ * Set-up: the first call on a device takes the array's address on that
+ * device and clears its counters with a fill kernel on the call's stream
+ * (the split leaves them zero after every call); PA_ERR_LAUNCH if that
+ * fails.  The call uses no hipMalloc, hipFree or allocating library
+ * routine.
+ * Concurrency: every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other host threads without
+ * ordering between them) race and give wrong rows; order them.
+ * ------------------------------------------------------------------------ */
+pa_status pa_decode_append_noalloc(const void* q, const void* k, const void* v, const int64_t* slot_mapping,
+                                   void* k_cache, void* v_cache, const int32_t* block_tables,
+                                   const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out,
+                                   void* stream, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                   pa_dtype dtype);
+
+/* ------------------------------------------------------------------------
  * Multi-token query over the paged cache: prefill, chunked prefill and
  * speculative verification.  Request b has L_b = seq_lens[b] tokens in the
  * cache, the last M_b of them new (their keys and values already written

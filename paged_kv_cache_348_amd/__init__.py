@@ -31,7 +31,7 @@ __all__ = [
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
     "new_workspace", "SharedPrefixPlan", "plan_shared_prefix", "decode_shared_prefix",
     "decode_shared_prefix_workspace_bytes", "shared_prefix_max_group", "simulate_memory", "PA_MEM_CONTIGUOUS",
-    "PA_MEM_PAGED", "swap_blocks", "decode_append", "prefill", "prefill_workspace_bytes", "prefill_path",
+    "PA_MEM_PAGED", "swap_blocks", "decode_append", "decode_append_noalloc", "prefill", "prefill_workspace_bytes", "prefill_path",
 ]
 
 
@@ -250,6 +250,39 @@ def decode_append(q, k, v, slot_mapping, k_cache, v_cache, block_tables, seq_len
                                  _dev(seq_lens, "seq_lens"), hkv, float(scale), _dev(out, "out"), _stream_ptr(stream),
                                  B, hq, d, bs, nb, mb, _dtype_code(q.dtype), _dev(workspace, "workspace"),
                                  workspace.numel() * workspace.element_size()), "pa_decode_append")
+    return out
+
+
+def decode_append_noalloc(q, k, v, slot_mapping, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int,
+                          scale: float, out, stream=None):
+    """decode_append without a workspace and without allocating
+    (pa_decode_append_noalloc): the library's static per-GPU scratch holds
+    the balanced split's counters and partials.  ``out`` must be given.
+    Calls that overlap on one GPU race (they share the scratch)."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    if hkv != num_kv_heads:
+        raise ValueError("num_kv_heads does not match the cache")
+    B, hq, dq = q.shape
+    if dq != d or q.dtype != k_cache.dtype:
+        raise ValueError("q must be [B, Hq, head_dim] in the cache dtype")
+    if tuple(k.shape) != (B, hkv, d) or k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B, num_kv_heads, head_dim] in the cache dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != B:
+        raise ValueError("slot_mapping must be int64 [B]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("seq_lens must be int32 [B]")
+    if out is None or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must be given and match q")
+    if B == 0:
+        return out
+    check(lib().pa_decode_append_noalloc(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), hkv, float(scale),
+        _dev(out, "out"), _stream_ptr(stream), B, hq, d, bs, nb, block_tables.shape[1], _dtype_code(q.dtype)),
+        "pa_decode_append_noalloc")
     return out
 
 

@@ -43,6 +43,9 @@ SIGNATURES = [
     ("pa_decode_append", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_int32, c_float, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                    c_int32, c_int32, c_int32, c_void_p, c_size_t]),
+    ("pa_decode_append_noalloc", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_int32, c_float, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                           c_int32, c_int32, c_int32, c_int32]),
     ("pa_decode_shared_prefix_workspace_bytes", c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                            c_int32]),
     ("pa_decode_shared_prefix", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float,

@@ -53,6 +53,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_decode_common.h"
@@ -844,6 +845,21 @@ __global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_balanced_k
     if constexpr (APPEND) append_rows<C::ES, D, BS>(ap, w, nwaves, B * Hkv, Hkv, lane);
 }
 
+// Zero n 32-bit words (a fill kernel rather than a memset, so that a caller
+// capturing the stream into a graph records a kernel node).
+__global__ __launch_bounds__(256) void zero_words_kernel(int32_t* __restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// Scratch of pa_decode_append_noalloc: the balanced split's merge counters
+// and cut-piece partials for callers that cannot allocate.  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code
+// never uses this name as an address: it takes each device's address of
+// the array from hipGetSymbolAddress (see noalloc_scratch below).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 }  // namespace pa
 
 // ---------------------------------------------------------------------------- host side
@@ -893,6 +909,32 @@ int balanced_waves() {
                       pa::kBalancedWavesPerGroup;
     }
     return cached[dev];
+}
+
+// Device address of the no-alloc scratch on the current device, set up on
+// the first call there: hipGetSymbolAddress with that device current, then
+// the counter region cleared by a fill kernel on the caller's stream (the
+// balanced split leaves its counters zero after every call, so once is
+// enough).  Null on failure.
+char* noalloc_scratch(hipStream_t stream) {
+    static std::mutex mu;
+    static char* addr[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(pa::scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        const int64_t words = (int64_t)(counter_bytes() / sizeof(int32_t));
+        hipLaunchKernelGGL(pa::zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                           reinterpret_cast<int32_t*>(p), words);
+        if (hipGetLastError() != hipSuccess) return nullptr;
+        addr[dev] = reinterpret_cast<char*>(p);
+    }
+    return addr[dev];
 }
 
 struct Launch {
@@ -975,7 +1017,8 @@ static pa_status decode_impl(const void* q, const void* k_cache, const void* v_c
                              const int32_t* seq_lens, int32_t num_kv_heads, float scale, void* out, void* stream,
                              int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t block_size,
                              int32_t num_blocks, int32_t max_blocks_per_seq, pa_dtype dtype, int32_t partition_size,
-                             void* workspace, size_t workspace_bytes, const pa::AppendArgs* ap) {
+                             void* workspace, size_t workspace_bytes, const pa::AppendArgs* ap,
+                             bool noalloc = false) {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
         partition_size < PA_PARTITION_BALANCED || !std::isfinite(scale))
         return PA_ERR_INVALID_ARG;
@@ -1006,7 +1049,21 @@ static pa_status decode_impl(const void* q, const void* k_cache, const void* v_c
         if (pmax > 65535) return PA_ERR_UNSUPPORTED;
     }
     Launch a{};
-    if (balanced || pmax > 1) {
+    if (noalloc) {
+        // the library's own scratch (pa_decode_append_noalloc): partials are
+        // indexed by wave, two slots of G rows per wave of the launch, so
+        // the size follows the device's wave count, not the batch
+        if (!balanced) return PA_ERR_INVALID_ARG;
+        const size_t rows = 2 * (size_t)balanced_waves() * (size_t)(num_q_heads / num_kv_heads);
+        const size_t o_bytes = align_up(rows * (size_t)head_dim * sizeof(float));
+        if (counter_bytes() + o_bytes + align_up(rows * 2 * sizeof(float)) > pa::kNoAllocScratchBytes)
+            return PA_ERR_UNSUPPORTED;
+        char* base = noalloc_scratch(reinterpret_cast<hipStream_t>(stream));
+        if (!base) return PA_ERR_LAUNCH;
+        a.counters = reinterpret_cast<int32_t*>(base);
+        a.po = reinterpret_cast<float*>(base + counter_bytes());
+        a.pml = reinterpret_cast<float*>(base + counter_bytes() + o_bytes);
+    } else if (balanced || pmax > 1) {
         const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                                       max_blocks_per_seq, partition_size);
         if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
@@ -1069,6 +1126,22 @@ extern "C" pa_status pa_decode_append(const void* q, const void* k, const void* 
     return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, stream, num_seqs,
                        num_q_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, dtype,
                        PA_PARTITION_BALANCED, workspace, workspace_bytes, &ap);
+}
+
+extern "C" pa_status pa_decode_append_noalloc(const void* q, const void* k, const void* v,
+                                              const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                              const int32_t* block_tables, const int32_t* seq_lens,
+                                              int32_t num_kv_heads, float scale, void* out, void* stream,
+                                              int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                              int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                              pa_dtype dtype) {
+    if (num_blocks < 0 || block_size <= 0) return PA_ERR_INVALID_ARG;
+    pa::AppendArgs ap{reinterpret_cast<const char*>(k), reinterpret_cast<const char*>(v), slot_mapping,
+                      reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache),
+                      (int64_t)num_blocks * block_size};
+    return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, stream, num_seqs,
+                       num_q_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, dtype,
+                       PA_PARTITION_BALANCED, nullptr, 0, &ap, true);
 }
 
 // ---- multi-token query on the balanced split (pa_prefill's path for
