@@ -324,6 +324,74 @@ def prefill_main(args, w):
     return 0
 
 
+def append_main(args, w):
+    """--append: pa_cache_write of every sequence's prefill tokens (positions
+    0 .. L-2, with the slots the allocator gave them and their own values) in
+    one call, timed with HIP events on the launch stream.  The writes repeat
+    the pool's contents, so it is unchanged.  Algorithmic bytes: each
+    token's keys and values read once and written once."""
+    import torch
+
+    import paged_kv_cache_348_amd as pa
+    from paged_kv_cache_348_amd.workload import build_device_batch, to_device
+
+    if any(op.kind == "fork" for op in w.ops):
+        print("--append takes workloads without shared blocks", file=sys.stderr)
+        return 2
+    dev = build_device_batch(w, device="cuda", partition_size=0)
+    bs = w.block_size
+    slots, ks, vs = [], [], []
+    for b in range(w.batch):
+        n = int(dev.host_lens[b]) - 1
+        if n <= 0:
+            continue
+        pos = np.arange(n)
+        slots.append(dev.host_tables[b][pos // bs].astype(np.int64) * bs + pos % bs)
+        k, v = w.token_kv(w.seq_ids[b], 0, n)
+        ks.append(k)
+        vs.append(v)
+    w.drop_kv()
+    T = int(sum(len(x) for x in slots))
+    sl = torch.from_numpy(np.concatenate(slots)).cuda()
+    kd = to_device(np.concatenate(ks), w.dtype, "cuda")
+    vd = to_device(np.concatenate(vs), w.dtype, "cuda")
+    del ks, vs
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pa.cache_write(kd, vd, sl, dev.k_cache, dev.v_cache)
+
+    for _ in range(args.warmup):
+        call()
+    runs = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        runs.append(a.elapsed_time(b) / args.steps)
+    ms = float(np.median(runs))
+    per_tok = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    algo = 2 * T * per_tok  # read + write
+    gbps = algo / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "bulk cache append (pa_cache_write) tokens/s on 1 MI355X",
+        "value": T / (ms * 1e-3), "unit": "appended tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (the workload's own prefill tokens and slots)",
+        "config": {"workload": WORKLOAD_TEXT.get(args.workload, w.name), "name": w.name, "tokens": T,
+                   "step": "pa_cache_write of every prefill token in one call"},
+        "roofline": {"bound": "hbm", "kernel": "pa_cache_write", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": algo},
+        "runs_ms": runs,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------------- GPU
 
 
@@ -533,6 +601,9 @@ def main(argv=None):
                     help="run only N decode launches of the step, each after a 1 GiB read that evicts L2 and "
                          "MALL, with no events around them (for a kernel trace of cold launches), then print "
                          "one JSON line")
+    ap.add_argument("--append", action="store_true",
+                    help="measure the bulk cache append instead: pa_cache_write of every sequence's prefill tokens "
+                         "(positions 0 .. L-2, their own slots and values) in one call")
     ap.add_argument("--prefill", type=int, default=0,
                     help="measure pa_prefill instead: the last N tokens of each request are new queries "
                          "(causal multi-token query: speculative verification, chunked prefill)")
@@ -551,6 +622,8 @@ def main(argv=None):
         w.free_order = np.arange(w.num_blocks, dtype=np.int32)
     if args.prefill > 0:
         return prefill_main(args, w)
+    if args.append:
+        return append_main(args, w)
     ps = args.partition_size
     mode = args.decode or DEFAULT_DECODE.get(args.workload, "split")
     if ps is None:

@@ -96,6 +96,22 @@ pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mappi
                          void* stream);
 
 /* ------------------------------------------------------------------------
+ * Host check of a slot mapping before an append (pa_cache_write,
+ * pa_decode_append): two tokens of one call writing one slot race on the
+ * device, and slots outside the pool are skipped there without notice.
+ * Pure host code, no GPU.
+ *
+ *   slot_mapping  host, int64 [num_tokens]; negative entries ("skip") pass
+ *   num_slots     num_blocks * block_size of the pool
+ *   first_bad     may be NULL; else the smallest index i whose slot lies in
+ *                 [num_slots, inf) or repeats a slot of an earlier index,
+ *                 or -1 when there is none
+ * Returns PA_OK, or PA_ERR_INVALID_ARG for such an entry, for num_tokens < 0,
+ * num_slots < 0, or a NULL slot_mapping with num_tokens > 0.
+ * ------------------------------------------------------------------------ */
+pa_status pa_check_slots(const int64_t* slot_mapping, int32_t num_tokens, int64_t num_slots, int32_t* first_bad);
+
+/* ------------------------------------------------------------------------
  * Copy whole physical blocks (keys and values of every kv-head): the copy
  * of a shared, partially filled block made before a request writes into it
  * (MCQ page, comparison table, "Copy on write blocks").

@@ -26,7 +26,7 @@ from ._lib import (PA_BF16, PA_PARTITION_BALANCED, PA_ERR_EXISTS, PA_ERR_INVALID
                    PA_ERR_UNSUPPORTED, PA_F32, PA_OK, P_I32, P_I64, PAError, check, lib, status_string)
 
 __all__ = [
-    "PAError", "Allocator", "cache_write", "copy_blocks", "decode", "decode_workspace_bytes", "new_kv_cache",
+    "PAError", "Allocator", "cache_write", "check_slots", "copy_blocks", "decode", "decode_workspace_bytes", "new_kv_cache",
     "kv_cache_shapes", "logical_view", "value_position", "stream_read", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_OOM",
     "PA_ERR_NOT_FOUND", "PA_ERR_LAUNCH", "PA_ERR_EXISTS", "PA_PARTITION_BALANCED", "status_string", "lib",
     "new_workspace", "SharedPrefixPlan", "plan_shared_prefix", "decode_shared_prefix",
@@ -147,6 +147,17 @@ def cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
     check(lib().pa_cache_write(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"),
                                _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), T, hkv, d, bs, nb,
                                _dtype_code(k.dtype), _stream_ptr(stream)), "pa_cache_write")
+
+
+def check_slots(slot_mapping, num_slots: int) -> None:
+    """Host check of an append's slots (pa_check_slots): raises PAError
+    naming the first repeated or out-of-pool entry.  Negative slots pass."""
+    sl = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int64).reshape(-1))
+    bad = ctypes.c_int32(-1)
+    st = lib().pa_check_slots(sl.ctypes.data_as(P_I64), sl.shape[0], int(num_slots), ctypes.byref(bad))
+    if st != PA_OK:
+        where = f"pa_check_slots (entry {bad.value}: slot {int(sl[bad.value])})" if bad.value >= 0 else "pa_check_slots"
+        raise PAError(st, where)
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:

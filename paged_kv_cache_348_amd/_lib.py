@@ -33,6 +33,7 @@ SIGNATURES = [
     ("pa_status_string", ctypes.c_char_p, [c_int32]),
     ("pa_cache_write", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                  c_int32, c_int32, c_int32, c_void_p]),
+    ("pa_check_slots", c_int32, [P_I64, c_int32, c_int64, P_I32]),
     ("pa_copy_blocks", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                  c_int32, c_void_p]),
     ("pa_decode_workspace_bytes", c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
@@ -87,15 +88,26 @@ class PAError(RuntimeError):
         super().__init__(f"{where}: {status_string(status)} (status {status})")
 
 
+# A host-only build of the library's C++ (allocator, planner, simulator,
+# slot checker) under the address and undefined-behaviour sanitizers
+# (``python -m paged_kv_cache_348_amd.build --sanitize``) is loaded instead
+# when this variable names it; its device entry points are absent.
+HOST_ONLY_ENV = "PA_HOST_ONLY_LIB"
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_348_amd.build`")
-        h = ctypes.CDLL(LIB_PATH)
+        host_only = os.environ.get(HOST_ONLY_ENV)
+        path = host_only or LIB_PATH
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m paged_kv_cache_348_amd.build`")
+        h = ctypes.CDLL(path)
         for name, res, args in SIGNATURES:
-            fn = getattr(h, name)
+            fn = getattr(h, name, None) if host_only else getattr(h, name)
+            if fn is None:
+                continue
             fn.restype = res
             fn.argtypes = args
         _lib = h

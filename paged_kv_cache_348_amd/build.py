@@ -1,9 +1,11 @@
 """Build libpa.so (the C-ABI library) in-tree for gfx950 with hipcc.
 
-    python -m paged_kv_cache_348_amd.build [--asm]
+    python -m paged_kv_cache_348_amd.build [--asm | --sanitize]
 
 Compiles every source under csrc/ into paged_kv_cache_348_amd/libpa.so.
 ``--asm`` also writes the device assembly of each HIP source under _build/.
+``--sanitize`` builds only the host C++ under ASan and UBSan into
+_build/libpa_host_sanitized.so (for the CPU tests marked host_lib).
 """
 from __future__ import annotations
 
@@ -78,6 +80,24 @@ def build(asm: bool = False, verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZED_HOST_LIB = os.path.join(ROOT, "_build", "libpa_host_sanitized.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized_host(out: str = SANITIZED_HOST_LIB) -> str:
+    """The library's host C++ alone (allocator, planner, memory simulator,
+    slot checker; no HIP code), built with g++ under AddressSanitizer and
+    UndefinedBehaviorSanitizer.  Load it through PA_HOST_ONLY_LIB with the
+    ASan runtime preloaded (``g++ -print-file-name=libasan.so``)."""
+    _, cpp = sources()
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    _run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-Wall", *SANITIZE_FLAGS, "-I", INCLUDE, *cpp, "-o", out])
+    return out
+
+
 if __name__ == "__main__":
-    path = build(asm="--asm" in sys.argv, verbose=True)
-    print(path)
+    if "--sanitize" in sys.argv:
+        print(build_sanitized_host())
+    else:
+        path = build(asm="--asm" in sys.argv, verbose=True)
+        print(path)

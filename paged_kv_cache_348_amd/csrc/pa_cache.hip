@@ -43,6 +43,157 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict
     store_token_chunk<ES, NT>(kc, vc, s, h, c, Hkv, D, BS, kv, vv);
 }
 
+// ---------------------------------------------------------------------------- bulk append
+//
+// An append of many tokens (a prefill) mostly fills whole blocks: BS
+// consecutive tokens whose slots are one block's slots in order.  For such a
+// block the (block, head) tiles of keys and values are written whole, as
+// consecutive 16-byte stores in tile order, so every store fills its share
+// of whole cache lines; the per-token path above writes each token's 16-byte
+// key chunks BS * 16 bytes apart and its values as 2-byte stores, leaving L2
+// to merge partial lines.
+//
+// A workgroup takes a window of W consecutive tokens of one kv-head.  It
+// owns every full block whose first token lies in the window (reading up to
+// BS - 1 tokens past it), and every token of the window that belongs to no
+// full block (written one token at a time, as above).  A token of a full
+// block whose first token lies in an earlier window is that window's.
+// Rows are staged through LDS with coalesced 16-byte loads; the LDS row
+// stride has 16 bytes of padding, so the tile-order reads of 16 lanes (one
+// token each) fall in different banks.
+template <int ES, int D, int BS>
+struct BulkCfg {
+    static constexpr int ROW = D * ES;          // bytes of one token's key (or value) row of one head
+    static constexpr int RS = ROW + 16;         // LDS row stride
+    static constexpr int CH = ROW / 16;         // 16-byte chunks of a row
+    static constexpr int W = 16384 / ROW;       // tokens of a window (16 KiB of keys)
+    static constexpr int ROWS = W + BS - 1;     // + the rest of a full block starting in the window
+    static constexpr int NS = W + 2 * (BS - 1);  // slots held: tokens t0 - (BS-1) .. t0 + W + BS - 2
+    static constexpr int X = 16 / ES;           // elements of a 16-byte piece
+    static constexpr int PIECES = D * BS * ES / 16;  // 16-byte pieces of a (block, head) tile
+    static constexpr int PR = BS * ES / 16;     // 16-byte pieces of one value row of a tile
+    static_assert(W % BS == 0 && W <= 256, "window");
+};
+
+template <int ES, int D, int BS>
+__global__ __launch_bounds__(256) void cache_write_bulk_kernel(const char* __restrict__ k,
+                                                               const char* __restrict__ v,
+                                                               const int64_t* __restrict__ slots,
+                                                               char* __restrict__ kc, char* __restrict__ vc,
+                                                               int64_t T, int Hkv, int64_t total_slots) {
+    using C = BulkCfg<ES, D, BS>;
+    __shared__ __align__(16) char lk[C::ROWS * C::RS];
+    __shared__ __align__(16) char lv[C::ROWS * C::RS];
+    __shared__ int64_t ls[C::NS];
+    __shared__ uint8_t need[C::ROWS];  // row r (token t0 + r) is read by this workgroup
+    __shared__ int lead[C::W / BS];    // window positions of the full blocks it owns
+    __shared__ int scat[C::W];         // window positions of its single tokens
+    __shared__ int n_lead, n_scat, n_rows;
+    const int tid = threadIdx.x;
+    const int h = blockIdx.y;
+    const int64_t t0 = (int64_t)blockIdx.x * C::W;
+
+    if (tid == 0) {
+        n_lead = 0;
+        n_scat = 0;
+        n_rows = 0;
+    }
+    for (int i = tid; i < C::NS; i += 256) {
+        const int64_t t = t0 - (BS - 1) + i;
+        const int64_t sl = (t >= 0 && t < T) ? slots[t] : -1;
+        ls[i] = (sl >= 0 && sl < total_slots) ? sl : -1;
+    }
+    for (int r = tid; r < C::ROWS; r += 256) need[r] = 0;
+    __syncthreads();
+
+    // slot index i = window position + BS - 1; a full block starts there when
+    // its slot is a block's first and the next BS - 1 tokens take the next slots
+    auto full_from = [&](int i) {
+        const int64_t s0 = ls[i];
+        if (s0 < 0 || s0 % BS != 0) return false;
+#pragma unroll
+        for (int q = 1; q < BS; ++q)
+            if (ls[i + q] != s0 + q) return false;
+        return true;
+    };
+    if (tid < C::W && t0 + tid < T) {
+        const int64_t s = ls[tid + BS - 1];
+        if (s >= 0) {
+            const int off = (int)(s % BS);
+            if (full_from(tid - off + BS - 1)) {  // in a full block
+                if (off == 0) {                   // ... whose first token is this one: owned here
+                    lead[atomicAdd(&n_lead, 1)] = tid;
+                    atomicMax(&n_rows, tid + BS);
+                    for (int q = 0; q < BS; ++q) need[tid + q] = 1;
+                }
+            } else {
+                scat[atomicAdd(&n_scat, 1)] = tid;
+                atomicMax(&n_rows, tid + 1);
+                need[tid] = 1;
+            }
+        }
+    }
+    __syncthreads();
+
+    // stage the rows this workgroup writes (keys and values of head h)
+    const int rows = n_rows;
+    for (int p = tid; p < rows * C::CH; p += 256) {
+        const int r = p / C::CH, c = p % C::CH;
+        if (!need[r]) continue;
+        const int64_t src = ((t0 + r) * Hkv + h) * (int64_t)C::ROW + c * 16;
+        const u32x4 kv = ld16(k + src);
+        const u32x4 vv = ld16(v + src);
+        *reinterpret_cast<u32x4*>(lk + r * C::RS + c * 16) = kv;
+        *reinterpret_cast<u32x4*>(lv + r * C::RS + c * 16) = vv;
+    }
+    __syncthreads();
+
+    // full blocks: both tiles whole, piece p of the tile at byte 16 p
+    const int nl = n_lead;
+    for (int li = 0; li < nl; ++li) {
+        const int j = lead[li];
+        const int64_t blk = ls[j + BS - 1] / BS;
+        const int64_t tile = (blk * Hkv + h) * (int64_t)D * BS * ES;  // byte offset of the (block, head) tile
+        for (int p = tid; p < C::PIECES; p += 256) {
+            // keys [D/X][BS][X]: piece p = (chunk p / BS, token p % BS)
+            const int c = p / BS, off = p % BS;
+            st16(kc + tile + (int64_t)p * 16, *reinterpret_cast<const u32x4*>(lk + (j + off) * C::RS + c * 16));
+            // values [D][BS]: piece p = (row p / PR, positions X (p % PR) ..)
+            const int d = p / C::PR, pos0 = (p % C::PR) * C::X;
+            u32x4 out;
+            if constexpr (ES == 2) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    // position pos holds the token of offset pos with bits 2 and 3
+                    // swapped (blocks of 16 or 32; the swap is its own inverse)
+                    auto tok = [&](int pos) {
+                        return BS >= 16 ? (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1) : pos;
+                    };
+                    const uint16_t lo = *reinterpret_cast<const uint16_t*>(lv + (j + tok(pos0 + e)) * C::RS + d * 2);
+                    const uint16_t hi =
+                        *reinterpret_cast<const uint16_t*>(lv + (j + tok(pos0 + e + 1)) * C::RS + d * 2);
+                    w[e / 2] = (uint32_t)lo | ((uint32_t)hi << 16);
+                }
+                out = u32x4{w[0], w[1], w[2], w[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = *reinterpret_cast<const uint32_t*>(lv + (j + pos0 + e) * C::RS + d * 4);
+            }
+            st16(vc + tile + (int64_t)p * 16, out);
+        }
+    }
+
+    // tokens in no full block: one token at a time
+    const int ns = n_scat;
+    for (int p = tid; p < ns * C::CH; p += 256) {
+        const int r = scat[p / C::CH], c = p % C::CH;
+        store_token_chunk<ES, false>(kc, vc, ls[r + BS - 1], h, c, Hkv, D, BS,
+                                     *reinterpret_cast<const u32x4*>(lk + r * C::RS + c * 16),
+                                     *reinterpret_cast<const u32x4*>(lv + r * C::RS + c * 16));
+    }
+}
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc,
                                                           const int32_t* __restrict__ pairs, int64_t block_bytes,
                                                           int num_blocks) {
@@ -114,6 +265,38 @@ inline pa_status check_pool(int32_t num_kv_heads, int32_t head_dim, int32_t bloc
 }
 }  // namespace
 
+namespace {
+template <int ES, int D, int BS>
+pa_status launch_bulk_t(const char* kp, const char* vp, const int64_t* slots, char* kcp, char* vcp, int64_t T,
+                        int Hkv, int64_t total_slots, hipStream_t s) {
+    using C = pa::BulkCfg<ES, D, BS>;
+    const dim3 grid((unsigned)((T + C::W - 1) / C::W), (unsigned)Hkv);
+    hipLaunchKernelGGL((pa::cache_write_bulk_kernel<ES, D, BS>), grid, dim3(256), 0, s, kp, vp, slots, kcp, vcp, T, Hkv,
+                       total_slots);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <int ES, int D>
+pa_status launch_bulk_d(int bs, const char* kp, const char* vp, const int64_t* slots, char* kcp, char* vcp,
+                        int64_t T, int Hkv, int64_t total_slots, hipStream_t s) {
+    switch (bs) {
+        case 8: return launch_bulk_t<ES, D, 8>(kp, vp, slots, kcp, vcp, T, Hkv, total_slots, s);
+        case 16: return launch_bulk_t<ES, D, 16>(kp, vp, slots, kcp, vcp, T, Hkv, total_slots, s);
+        default: return launch_bulk_t<ES, D, 32>(kp, vp, slots, kcp, vcp, T, Hkv, total_slots, s);
+    }
+}
+
+// Arguments were validated by pa_cache_write.
+pa_status launch_bulk(pa_dtype dtype, int head_dim, int bs, const char* kp, const char* vp, const int64_t* slots,
+                      char* kcp, char* vcp, int64_t T, int Hkv, int64_t total_slots, hipStream_t s) {
+    if (dtype == PA_BF16)
+        return head_dim == 128 ? launch_bulk_d<2, 128>(bs, kp, vp, slots, kcp, vcp, T, Hkv, total_slots, s)
+                               : launch_bulk_d<2, 64>(bs, kp, vp, slots, kcp, vcp, T, Hkv, total_slots, s);
+    return head_dim == 128 ? launch_bulk_d<4, 128>(bs, kp, vp, slots, kcp, vcp, T, Hkv, total_slots, s)
+                           : launch_bulk_d<4, 64>(bs, kp, vp, slots, kcp, vcp, T, Hkv, total_slots, s);
+}
+}  // namespace
+
 extern "C" pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
                                     void* v_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
@@ -135,8 +318,13 @@ extern "C" pa_status pa_cache_write(const void* k, const void* v, const int64_t*
     char* kcp = reinterpret_cast<char*>(k_cache);
     char* vcp = reinterpret_cast<char*>(v_cache);
     // decode-sized appends (about one token per block) store non-temporally,
-    // bulk appends through write-back (see store_token_chunk)
-    const bool nt = num_tokens <= kNonTemporalMaxTokens;
+    // one thread per 16-byte chunk; bulk appends write whole tiles
+    if (num_tokens > kNonTemporalMaxTokens) {
+        if ((int64_t)num_tokens / 16 + 1 > 2147483647LL || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+        return launch_bulk(dtype, head_dim, block_size, kp, vp, slot_mapping, kcp, vcp, num_tokens, num_kv_heads,
+                           total_slots, s);
+    }
+    const bool nt = true;
     if (dtype == PA_BF16) {
         if (nt)
             hipLaunchKernelGGL((pa::cache_write_kernel<2, true>), dim3((unsigned)grid), dim3(256), 0, s, kp, vp,

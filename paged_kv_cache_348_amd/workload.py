@@ -16,7 +16,8 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-from . import (PA_PARTITION_BALANCED, Allocator, cache_write, copy_blocks, decode, decode_append, decode_shared_prefix,
+from . import (PA_PARTITION_BALANCED, Allocator, cache_write, check_slots, copy_blocks, decode, decode_append,
+               decode_shared_prefix,
                decode_shared_prefix_workspace_bytes, decode_workspace_bytes, new_kv_cache, new_workspace,
                plan_shared_prefix, shared_prefix_max_group)
 
@@ -163,7 +164,9 @@ class _Batcher:
             copy_blocks(self.kc, self.vc, pairs)
             self.launches["copy_blocks"] += 1
         if self.slots:
-            slots = torch.from_numpy(np.concatenate(self.slots).astype(np.int64)).to(self.device)
+            host = np.concatenate(self.slots).astype(np.int64)
+            check_slots(host, self.w.num_blocks * self.w.block_size)  # distinct, inside the pool
+            slots = torch.from_numpy(host).to(self.device)
             k = to_device(np.concatenate(self.ks), self.w.dtype, self.device)
             v = to_device(np.concatenate(self.vs), self.w.dtype, self.device)
             cache_write(k, v, slots, self.kc, self.vc)
@@ -228,6 +231,7 @@ def build_device_batch(w, device="cuda", partition_size: Optional[int] = None, n
     # decode-step tokens, in batch order (sequences without one are skipped)
     rows = [b for b, s in enumerate(w.seq_ids) if s in dec]
     dslots = np.array([dec[w.seq_ids[b]] for b in rows], dtype=np.int64)
+    check_slots(dslots, w.num_blocks * w.block_size)
     dk, dv = [], []
     for b in rows:  # the decode token is the last position, L - 1
         k, v = w.token_kv(w.seq_ids[b], int(lens[b]) - 1, 1)

@@ -11,6 +11,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workloads (minutes on the CPU side)")
+    config.addinivalue_line("markers", "host_lib: uses only libpa's host C++ (allocator, planner, memory "
+                                       "simulator, slot checker); also run against the sanitized host build")
 
 
 def pytest_collection_modifyitems(config, items):

@@ -39,6 +39,7 @@ def test_library_exports_every_declared_function():
     assert sorted(n for n, _, _ in _lib.SIGNATURES) == names
 
 
+@pytest.mark.host_lib
 def test_status_strings():
     for code in range(7):
         assert pa.status_string(code) not in ("", "?", "unknown status")
@@ -201,6 +202,7 @@ def replay_both(w):
     return m, a, live
 
 
+@pytest.mark.host_lib
 @pytest.mark.parametrize("name,kw", [
     ("tiny", {}),
     ("llama3_8b", {}),
@@ -220,6 +222,7 @@ def test_allocator_matches_model_on_workloads(name, kw):
         assert lens[b] == m.lens[s] == w.seq_lens[b]
 
 
+@pytest.mark.host_lib
 @pytest.mark.parametrize("seed", range(6))
 def test_allocator_matches_model_on_random_traces(seed):
     rng = random.Random(100 + seed)
@@ -262,6 +265,7 @@ def test_allocator_matches_model_on_random_traces(seed):
                                              list(m.ref), list(m.free))
 
 
+@pytest.mark.host_lib
 def test_allocator_error_codes():
     a = pa.Allocator(4, 2)
     with pytest.raises(pa.PAError) as e:
@@ -373,6 +377,7 @@ def plan(tables, lens, bs=16, mg=8, mins=1):
     return [tuple(g) for g in p.groups.tolist()], p.prefix_blocks.tolist(), p.max_group, p.max_prefix_blocks
 
 
+@pytest.mark.host_lib
 def test_plan_groups_requests_with_common_leading_blocks():
     # three requests share blocks 5, 6, 7; the fourth shares nothing
     t = [[5, 6, 7, 10], [5, 6, 7, 11], [5, 6, 7, 12], [9, 1, 2, 3]]
@@ -391,6 +396,7 @@ def test_plan_groups_requests_with_common_leading_blocks():
     assert plan([[1, 2]], [32]) == ([], [0], 1, 0)
 
 
+@pytest.mark.host_lib
 def test_plan_stops_when_a_join_would_save_fewer_reads():
     # A and B share 10 blocks; C shares 2 with them: (2 members, 10 blocks) saves 10 reads,
     # (3 members, 2 blocks) would save 4, so C starts its own group with D
@@ -406,6 +412,7 @@ def test_plan_stops_when_a_join_would_save_fewer_reads():
     assert g == [(0, 3)] and p == [9, 9, 9]
 
 
+@pytest.mark.host_lib
 def test_plan_on_the_prefix_sharing_workload():
     w = make_workload("prefix_share", seed=0, prompts=4, samples=8, prompt_len=2040, tail_max=40)
     a = pa.Allocator(w.num_blocks, w.block_size, w.free_order)
@@ -423,6 +430,7 @@ def test_plan_on_the_prefix_sharing_workload():
     assert g == [(8 * i, 8) for i in range(4)] and p == [127] * 32 and mg == 8 and mp == 127
 
 
+@pytest.mark.host_lib
 def test_plan_rejects_bad_arguments():
     t = np.zeros((2, 3), np.int32)
     ln = np.zeros(2, np.int32)

@@ -99,6 +99,7 @@ def test_the_pages_headline_claim_qualitatively():
 
 
 # ---------------------------------------------------------------- library simulator vs oracle
+@pytest.mark.host_lib
 @pytest.mark.parametrize("seed", range(3))
 @pytest.mark.parametrize("scheme,param", [(C, 2048), (C, 700), (P, 1), (P, 8), (P, 16), (P, 64)])
 def test_library_simulator_matches_oracle(seed, scheme, param):
@@ -109,6 +110,7 @@ def test_library_simulator_matches_oracle(seed, scheme, param):
         assert got == want, (seed, scheme, param, cap)
 
 
+@pytest.mark.host_lib
 def test_library_simulator_edge_cases():
     # empty trace, idle gaps between arrivals, zero replies, a pool smaller than one block
     assert pa.simulate_memory([], [], [], 100, pa.PA_MEM_PAGED, 16)["steps"] == 0
@@ -117,6 +119,7 @@ def test_library_simulator_edge_cases():
         assert pa.simulate_memory(*args) == om.simulate(*args), args
 
 
+@pytest.mark.host_lib
 @pytest.mark.parametrize("args", [
     ([0, 1], [5, 0], [1, 1], 100, 1, 4),       # empty prompt
     ([1, 0], [5, 5], [1, 1], 100, 1, 4),       # arrivals out of order

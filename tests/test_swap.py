@@ -110,6 +110,7 @@ def test_round_trip_keeps_every_token_and_the_sharing():
     assert dev.tables[0][: len(hb)] == dev.tables[1][: len(hb)] == dev.tables[2][: len(hb)]
 
 
+@pytest.mark.host_lib
 @pytest.mark.parametrize("seed", range(6))
 def test_library_move_matches_model_on_random_traces(seed):
     rng = random.Random(500 + seed)
@@ -168,6 +169,7 @@ def test_library_move_matches_model_on_random_traces(seed):
                                               list(mm.ref), list(mm.free))
 
 
+@pytest.mark.host_lib
 def test_move_errors_change_nothing():
     a, h = pa.Allocator(6, 2), pa.Allocator(2, 2)
     a.add_seq(1)
