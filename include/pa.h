@@ -275,7 +275,7 @@ pa_status pa_decode_append_noalloc(const void* q, const void* k, const void* v, 
  *                tile of query tokens, request) walks all of each tile's
  *                keys; for bfloat16 chunks of max_query_len * (num_q_heads /
  *                num_kv_heads) >= 128 columns (block size 16 or 32, or head
- *                dim 64), workgroups of four such tiles walk them together,
+ *                dim 64; scale > 0), workgroups of four such tiles walk them together,
  *                each key/value step read from the pool once and shared
  *                through LDS.  The same holds with a workspace when
  *                neither path below applies (see pa_prefill_workspace_bytes).

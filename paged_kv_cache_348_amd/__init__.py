@@ -316,7 +316,26 @@ class SharedPrefixPlan:
     def num_groups(self) -> int:
         return int(self.groups.shape[0])
 
+    def check(self) -> None:
+        """The plan's invariant (what pa_plan_shared_prefix returns): groups
+        lie in the batch and do not overlap, and every request whose
+        prefix_blocks is in 1 .. max_prefix_blocks lies in a group (else its
+        rows would be unspecified).  Raises ValueError."""
+        B = int(self.prefix_blocks.shape[0])
+        owner = np.full(B, -1, dtype=np.int64)
+        for i, (s0, n) in enumerate(np.asarray(self.groups, dtype=np.int64).reshape(-1, 2)):
+            if s0 < 0 or n < 1 or s0 + n > B:
+                raise ValueError(f"group {i} ({s0}, {n}) is outside the batch of {B}")
+            if (owner[s0:s0 + n] >= 0).any():
+                raise ValueError(f"group {i} overlaps another group")
+            owner[s0:s0 + n] = i
+        pb = np.asarray(self.prefix_blocks)
+        loose = np.nonzero((pb > 0) & (pb <= self.max_prefix_blocks) & (owner < 0))[0]
+        if len(loose):
+            raise ValueError(f"request {int(loose[0])} has shared prefix blocks but no group")
+
     def to(self, device="cuda"):
+        self.check()
         torch = _torch()
         g = self.groups if self.num_groups else np.zeros((1, 2), dtype=np.int32)
         self.d_groups = torch.from_numpy(np.ascontiguousarray(g)).to(device)
@@ -431,12 +450,12 @@ PREFILL_WORKGROUP_COLUMNS = 128
 
 
 def prefill_path(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_query_len: int, workspace_bytes: int,
-                 bf16: bool = True, head_dim: int = 128, block_size: int = 16) -> str:
+                 bf16: bool = True, head_dim: int = 128, block_size: int = 16, scale: float = 1.0) -> str:
     """Which path pa_prefill takes given a workspace of ``workspace_bytes``
     sized by prefill_workspace_bytes (a description for logs)."""
     if not workspace_bytes:
-        # (blocks of 8 with head dim 128 keep the query tiles)
-        if (bf16 and not (head_dim == 128 and block_size == 8)
+        # (blocks of 8 with head dim 128, and scales <= 0, keep the query tiles)
+        if (bf16 and scale > 0 and not (head_dim == 128 and block_size == 8)
                 and max_query_len * (num_q_heads // num_kv_heads) >= PREFILL_WORKGROUP_COLUMNS):
             return "workgroup tiles"
         return "query tiles"

@@ -209,7 +209,11 @@ __device__ __forceinline__ void rescale(float& m_run, float& l_run, f32x4 (&acc)
 // sees the keys up to its own position); Lmin is the smallest limit of the
 // wave's columns, so steps wholly below it skip the masking.  Values are
 // still zeroed only at or past L (everything below L is stored data).
-template <bool BF16, int D, int BS, bool CAUSAL = false>
+// FMA_EXP (bfloat16, scale_log2 > 0 only): the scores stay unscaled, their
+// maximum is scaled once, and each probability is 2^fma(s, scale_log2, -m):
+// the same running maximum (rounding is monotonic for a positive factor)
+// for one instruction per score instead of two.
+template <bool BF16, int D, int BS, bool CAUSAL = false, bool FMA_EXP = false>
 __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
                                              const u32x4 (&qr)[DecodeCfg<BF16, D, BS>::NKC], float& m_run,
                                              float& l_run, f32x4 (&acc)[DecodeCfg<BF16, D, BS>::NV], int tok0,
@@ -232,8 +236,8 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
         float s[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s[i] = sa[i] * scale_log2;
-            s[4 + i] = sb[i] * scale_log2;
+            s[i] = FMA_EXP ? sa[i] : sa[i] * scale_log2;
+            s[4 + i] = FMA_EXP ? sb[i] : sb[i] * scale_log2;
         }
         if (tail) {
             // element e of the lane's scores / value operand is token tok(e)
@@ -259,6 +263,7 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
         mx = wave_max16(mx);
+        if constexpr (FMA_EXP) mx *= scale_log2;
         rescale<C::NV>(m_run, l_run, acc, mx);
         // causal: a run cut mid-sequence can start with steps whose keys are all
         // past a column's position; that column keeps m = -inf and gets p = 0
@@ -267,7 +272,7 @@ __device__ __forceinline__ void compute_step(StepRegs<BF16, D, BS>& cur,
         float rs = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            pe[e] = __builtin_amdgcn_exp2f(s[e] - mref);
+            pe[e] = __builtin_amdgcn_exp2f(FMA_EXP ? __builtin_fmaf(s[e], scale_log2, -mref) : s[e] - mref);
             rs += pe[e];
         }
         rs = wave_sum16(rs);

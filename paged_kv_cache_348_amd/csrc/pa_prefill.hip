@@ -259,8 +259,26 @@ __global__ __launch_bounds__(1024) void prefill_merge_kernel(const float* __rest
 // wave, and two waves fit a SIMD (at most 256 registers each), so one
 // wave's softmax work overlaps the other's matrix-core work.
 
+// s_waitcnt immediate (gfx9 encoding) that waits for at most n outstanding
+// vector-memory loads and leaves the export and LDS/scalar counters alone.
+constexpr int vmcnt_only(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+// Workgroup barrier of the LDS ring: this wave's direct loads but the last
+// IN_FLIGHT have landed, then every wave meets.  A __syncthreads() would
+// add a workgroup release fence, which waits for every direct load still
+// landing (they count as LDS stores); the compiler fences here only keep
+// the compiler from moving memory accesses across the barrier.
+template <int IN_FLIGHT>
+__device__ __forceinline__ void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(IN_FLIGHT));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int D, int BS, int NW>
 struct FlashCfg {
+    static constexpr int NSLOT = 4;          // ring slots: two steps resident, two in flight
     static constexpr int TILE = D * BS * 2;  // bytes of one (block, head) tile
     static constexpr int PAD = 128;          // LDS gap after each tile (the two tiles a lane group reads differ in bank)
     static constexpr int TSTRIDE = TILE + PAD;
@@ -273,17 +291,6 @@ struct FlashCfg {
     // (values), in tile blk(w, i) of the step
     __device__ static int blk(int w, int i) { return 1024 * (w + NW * i) / TILE; }
     __device__ static int inner(int w, int i) { return 1024 * (w + NW * i) - blk(w, i) * TILE; }
-};
-
-template <int NLD>
-struct FlashStage {
-    u32x4 k[NLD];
-    u32x4 v[NLD];
-};
-
-template <int NLD>
-struct FlashEnt {
-    int32_t e[NLD];
 };
 
 // LDS byte offsets (within a slot's key or value region) of a lane's
@@ -313,35 +320,107 @@ struct FlashOffsets {
     }
 };
 
+// A step's keys (both 16-token tiles) and values from a ring slot, in the
+// matrix-core operand order.
 template <int D, int BS, int TSTRIDE>
-__device__ __forceinline__ void flash_read_step(StepRegs<true, D, BS>& r, const char* sk, const char* sv,
+__device__ __forceinline__ void flash_read_keys(u32x4 (&k)[2][D / 32], const char* sk,
                                                 const FlashOffsets<D, BS, TSTRIDE>& o) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) k[t][c] = *reinterpret_cast<const u32x4*>(sk + o.k[t] + 4 * c * BS * 16);
+}
+
+template <int D, int BS, int TSTRIDE>
+__device__ __forceinline__ void flash_read_values(u32x4 (&v)[D / 16], const char* sv,
+                                                  const FlashOffsets<D, BS, TSTRIDE>& o) {
     using C = DecodeCfg<true, D, BS>;
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-        for (int c = 0; c < C::NKC; ++c)
-            r.k[t][c] = *reinterpret_cast<const u32x4*>(sk + o.k[t] + 4 * c * BS * 16);
     if constexpr (C::VIL) {
 #pragma unroll
-        for (int c = 0; c < C::NV; ++c) r.v[c] = *reinterpret_cast<const u32x4*>(sv + o.va + 16 * c * BS * 2);
+        for (int c = 0; c < C::NV; ++c) v[c] = *reinterpret_cast<const u32x4*>(sv + o.va + 16 * c * BS * 2);
     } else {
 #pragma unroll
         for (int c = 0; c < C::NV; ++c) {
             const u32x2 lo = *reinterpret_cast<const u32x2*>(sv + o.va + 16 * c * BS * 2);
             const u32x2 hi = *reinterpret_cast<const u32x2*>(sv + o.vb + 16 * c * BS * 2);
-            r.v[c] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            v[c] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
     }
+}
+
+// Step token held in element e (scores and value operand) of lane group j.
+template <int BS>
+__device__ __forceinline__ int flash_tok(int tok0, int j, int e) {
+    return BS >= 16 ? tok0 + 16 * (j >> 1) + 4 * (j & 1) + (e & 3) + 8 * (e >> 2)
+                    : tok0 + 4 * j + (e & 3) + 16 * (e >> 2);
+}
+
+// Scores of one 16-column tile for a step's 32 keys (unscaled): sa for the
+// keys of tile 0, sb for tile 1, lane (n, j) holding rows 4 j .. 4 j + 3.
+template <int D>
+__device__ __forceinline__ void flash_scores(f32x4& sa, f32x4& sb, const u32x4 (&k)[2][D / 32],
+                                             const u32x4 (&q)[D / 32]) {
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[0][0]), __builtin_bit_cast(bf16x8, q[0]),
+                                                 f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[1][0]), __builtin_bit_cast(bf16x8, q[0]),
+                                                 f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int c = 1; c < D / 32; ++c) {
+        const bf16x8 qv = __builtin_bit_cast(bf16x8, q[c]);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[0][c]), qv, sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[1][c]), qv, sb, 0, 0, 0);
+    }
+}
+
+// Online-softmax update and PV of one tile from its step scores, as
+// compute_step does (base 2, lazy rescale), with the scale folded into the
+// exponent argument (scale_log2 > 0) and the causal mask per lane column
+// (limit Lcol) on a tail step (tail: some column's limit falls inside the
+// step, a wave-uniform test).  v: the step's values, already zeroed at or
+// past the keys' end.
+template <int D, int BS>
+__device__ __forceinline__ void flash_softmax_pv(RunState<true, D, BS>& S, f32x4 sa, f32x4 sb,
+                                                 const u32x4 (&v)[D / 16], int tok0, int j, float sl2, int Lcol,
+                                                 bool tail) {
+    float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+    if (tail) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = flash_tok<BS>(tok0, j, e) < Lcol ? s[e] : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+    mx = wave_max16(mx) * sl2;
+    rescale<D / 16>(S.m, S.l, S.acc, mx);
+    // a column with no visible key yet keeps m = -inf and gets p = 0
+    const float mref = S.m == -INFINITY ? 0.0f : S.m;
+    float pe[8];
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -mref));
+        rs += pe[e];
+    }
+    S.l += wave_sum16(rs);
+    const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]), pack_bf16x2(pe[4], pe[5]),
+                      pack_bf16x2(pe[6], pe[7])};
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        S.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[c]), pb, S.acc[c], 0, 0, 0);
 }
 
 template <int D, int BS, int NW, int NCT>
 struct FlashWave {
     using C = DecodeCfg<true, D, BS>;
     using F = FlashCfg<D, BS, NW>;
-    using Stage = FlashStage<F::NLD>;
-    using Ent = FlashEnt<F::NLD>;
-    char* lds;  // two slots of [keys SLOT | values SLOT]
+    // the ring: NSLOT slots of [keys SLOT | values SLOT], each its own LDS
+    // array, so the compiler can tell a slot's reads from the direct loads
+    // still landing in the other slots and does not wait for those
+    char* r0;
+    char* r1;
+    char* r2;
+    char* r3;
     const char* kbase;
     const char* vbase;
     const int32_t* trow;
@@ -354,58 +433,76 @@ struct FlashWave {
     u32x4 qr[NCT][C::NKC];
     RunState<true, D, BS> S[NCT];
 
-    // table entries of this lane's pieces of step y (vector loads: their wait
-    // is ordered with the key/value loads, see above)
-    __device__ __forceinline__ void ent(Ent& E, int y) {
-#pragma unroll
-        for (int i = 0; i < F::NLD; ++i) E.e[i] = trow[min(y * 32 / BS + F::blk(w, i), lastb)];
+    template <int SL>
+    __device__ __forceinline__ char* slot_keys() {
+        static_assert(F::NSLOT == 4 && SL >= 0 && SL < 4, "four ring slots");
+        return SL == 0 ? r0 : SL == 1 ? r1 : SL == 2 ? r2 : r3;
     }
-    __device__ __forceinline__ void issue(Stage& R, const Ent& E) {
+
+    // Table entry of this wave's piece i of step y (wave-uniform: a scalar
+    // load; steps past the keys repeat the last block).
+    __device__ __forceinline__ int32_t entry(int y, int i) { return trow[min(y * 32 / BS + F::blk(w, i), lastb)]; }
+
+    // Copy this wave's pieces of step y (entries e[]) from the pool into its
+    // ring slot, straight into LDS (no registers): each instruction moves
+    // 1 KiB, 16 bytes per lane at consecutive addresses on both sides.
+    template <int SL>
+    __device__ __forceinline__ void issue(const int32_t (&e)[F::NLD]) {
+        char* sk = slot_keys<SL>();
 #pragma unroll
         for (int i = 0; i < F::NLD; ++i) {
-            const int32_t e = E.e[i];
-            const bool ok = e >= 0 && e < num_blocks;
+            const bool ok = e[i] >= 0 && e[i] < num_blocks;
             bad |= !ok;
-            // the piece's base is wave-uniform (scalar registers); the lane's
-            // 16 bytes are added last, as the load's vector offset
-            const uint64_t o = (uint64_t)(uint32_t)(ok ? e : 0) * blk_bytes + (uint32_t)F::inner(w, i);
-            R.k[i] = ld16(kbase + o + 16 * lane);
-            R.v[i] = ld16(vbase + o + 16 * lane);
+            const uint64_t o = (uint64_t)(uint32_t)(ok ? e[i] : 0) * blk_bytes + (uint32_t)F::inner(w, i);
+            const int lo = F::blk(w, i) * F::TSTRIDE + F::inner(w, i);
+            __builtin_amdgcn_global_load_lds(kbase + o + 16 * lane,
+                                             (__attribute__((address_space(3))) void*)(sk + lo), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vbase + o + 16 * lane,
+                                             (__attribute__((address_space(3))) void*)(sk + F::SLOT + lo), 16, 0, 0);
         }
     }
-    __device__ __forceinline__ void put(const Stage& R, int slot) {
-        char* sk = lds + slot * 2 * F::SLOT;
+
+    // Iteration x: step x + 1's scores into `nxt` (their matrix-core work
+    // runs while this step's softmax goes on), step x's softmax and PV from
+    // `cur`, then the ring turn: wait for step x + 2's pieces, one barrier
+    // (step x + 2 visible to every wave, slot x free), step x + 4's pieces
+    // into slot x.  Memory operations are the same on every path (past the
+    // keys the entries repeat the last block), so each wait leaves the later
+    // step's loads in flight.
+    // (x is in slot SL = x % 4)
+    template <int SL>
+    __device__ __forceinline__ void iter(int x, f32x4 (&cur)[NCT][2], f32x4 (&nxt)[NCT][2]) {
+        int32_t e[F::NLD];
 #pragma unroll
-        for (int i = 0; i < F::NLD; ++i) {
-            const int o = F::blk(w, i) * F::TSTRIDE + F::inner(w, i) + 16 * lane;
-            *reinterpret_cast<u32x4*>(sk + o) = R.k[i];
-            *reinterpret_cast<u32x4*>(sk + F::SLOT + o) = R.v[i];
+        for (int i = 0; i < F::NLD; ++i) e[i] = entry(x + 4, i);
+        u32x4 k[2][C::NKC];
+        flash_read_keys<D, BS, F::TSTRIDE>(k, slot_keys<(SL + 1) % 4>(), off);
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) flash_scores<D>(nxt[t][0], nxt[t][1], k, qr[t]);
+        if (x < nst) {
+            u32x4 v[C::NV];
+            flash_read_values<D, BS, F::TSTRIDE>(v, slot_keys<SL>() + F::SLOT, off);
+            const int tok0 = 32 * x;
+            if (tok0 + 32 > kend) {  // the last step: values at or past the keys' end may be anything
+                uint32_t keep[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    keep[q] = (flash_tok<BS>(tok0, j, 2 * q) < kend ? 0x0000ffffu : 0u) |
+                              (flash_tok<BS>(tok0, j, 2 * q + 1) < kend ? 0xffff0000u : 0u);
+#pragma unroll
+                for (int c = 0; c < C::NV; ++c)
+                    v[c] = u32x4{v[c][0] & keep[0], v[c][1] & keep[1], v[c][2] & keep[2], v[c][3] & keep[3]};
+            }
+#pragma unroll
+            for (int t = 0; t < NCT; ++t)
+                flash_softmax_pv<D, BS>(S[t], cur[t][0], cur[t][1], v, tok0, j, sl2, Lcol[t], tok0 + 32 > Lmin[t]);
         }
-    }
-    __device__ __forceinline__ void compute(int x, int slot) {
-        StepRegs<true, D, BS> cur;
-        const char* sk = lds + slot * 2 * F::SLOT;
-        flash_read_step<D, BS, F::TSTRIDE>(cur, sk, sk + F::SLOT, off);
-#pragma unroll
-        for (int t = 0; t < NCT; ++t)
-            compute_step<true, D, BS, true>(cur, qr[t], S[t].m, S[t].l, S[t].acc, 32 * x, kend, j, sl2, Lcol[t],
-                                            Lmin[t]);
-    }
-    // step x of the loop; Sn holds step x + 1, En the entries of step x + 3,
-    // Ex is free for step x + 4's entries.  Loads and ring writes happen
-    // whether or not their step exists (past the last step the entries repeat
-    // the last block, and a slot written past the end is never read): the
-    // same sequence of memory operations on every path lets each wait leave
-    // the later steps' loads in flight.
-    __device__ __forceinline__ void step(int x, int slot, Stage& Sn, Ent& Ex,
-                                         const Ent& En) {
-        if (x < nst) compute(x, slot);  // (the pair loop's extra step computes nothing)
-        put(Sn, slot ^ 1);
-        __syncthreads();
-        ent(Ex, x + 4);
-        __builtin_amdgcn_sched_barrier(0);  // the entries are issued before the step that does not need them
-        issue(Sn, En);
-        __builtin_amdgcn_sched_barrier(0);
+        // step x + 2's pieces have landed once at most step x + 3's (2 NLD
+        // loads) are outstanding; the barrier makes every wave's visible and
+        // tells every wave that slot x (read above, its values consumed by the
+        // PV products, and one iteration ago) is free
+        ring_barrier<2 * F::NLD>();
+        issue<SL>(e);
     }
 };
 
@@ -418,7 +515,10 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
     using C = DecodeCfg<true, D, BS>;
     using F = FlashCfg<D, BS, NW>;
     using W_t = FlashWave<D, BS, NW, NCT>;
-    __shared__ __attribute__((aligned(16))) char lds[4 * F::SLOT];
+    __shared__ __attribute__((aligned(16))) char ring0[2 * F::SLOT];
+    __shared__ __attribute__((aligned(16))) char ring1[2 * F::SLOT];
+    __shared__ __attribute__((aligned(16))) char ring2[2 * F::SLOT];
+    __shared__ __attribute__((aligned(16))) char ring3[2 * F::SLOT];
     __shared__ int s_bad;
     const int g = blockIdx.x;
     const int qt = blockIdx.y;
@@ -445,7 +545,10 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
     const int kend = L - M + q0 + min(QTW, M - q0);  // keys of the workgroup: [0, kend)
 
     W_t W;
-    W.lds = lds;
+    W.r0 = ring0;
+    W.r1 = ring1;
+    W.r2 = ring2;
+    W.r3 = ring3;
     W.w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: entry loads and piece bases go scalar
     W.lane = tid & 63;
     W.n = W.lane & 15;
@@ -479,36 +582,46 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
 #pragma unroll
         for (int k = 0; k < C::NKC; ++k) W.qr[t][k] = ld16(qp + (int64_t)(4 * k + W.j) * 16);
         W.Lcol[t] = min(L - M + tok + 1, kend);
-        W.Lmin[t] = nqw > 0 ? min(pos0 + (16 * t) / G + 1, kend) : W.Lcol[t];
+        // smallest key limit of the tile's columns, wave-uniform so the tail
+        // test is a scalar branch (a wave past the request's tokens: every
+        // step is a tail, each lane masked by its own limit)
+        W.Lmin[t] = __builtin_amdgcn_readfirstlane(nqw > 0 ? min(pos0 + (16 * t) / G + 1, kend) : 0);
         run_init(W.S[t]);
     }
 
-    // prologue: step 0 in slot 0, steps 1 and 2 in flight, step 3's entries
-    // in flight (steps past the last one load the last block again)
-    typename W_t::Stage SA, SB;
-    typename W_t::Ent EA, EB;
-    const int nst = W.nst;
-    W.ent(EA, 0);
-    W.ent(EB, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    W.issue(SA, EA);
-    __builtin_amdgcn_sched_barrier(0);
-    W.ent(EA, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    W.issue(SB, EB);
-    __builtin_amdgcn_sched_barrier(0);
-    W.ent(EB, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    W.put(SA, 0);
-    __syncthreads();
-    W.issue(SA, EA);
-    __builtin_amdgcn_sched_barrier(0);
-    // steps in pairs; an odd count ends with one step past the keys, which
-    // only keeps the loads and ring writes in step
-    for (int x = 0; x < nst; x += 2) {
-        W.step(x, 0, SB, EA, EB);
-        W.step(x + 1, 1, SA, EB, EA);
+    // prologue: steps 0 .. 3 into slots 0 .. 3; wait for 0 and 1 (2 and 3
+    // stay in flight); step 0's scores
+    {
+        int32_t e[F::NSLOT][F::NLD];
+#pragma unroll
+        for (int y = 0; y < F::NSLOT; ++y)
+#pragma unroll
+            for (int i = 0; i < F::NLD; ++i) e[y][i] = W.entry(y, i);
+        W.template issue<0>(e[0]);
+        W.template issue<1>(e[1]);
+        W.template issue<2>(e[2]);
+        W.template issue<3>(e[3]);
     }
+    ring_barrier<2 * 2 * F::NLD>();
+    f32x4 SA[NCT][2], SB[NCT][2];
+    {
+        u32x4 k[2][C::NKC];
+        flash_read_keys<D, BS, F::TSTRIDE>(k, W.template slot_keys<0>(), W.off);
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) flash_scores<D>(SA[t][0], SA[t][1], k, W.qr[t]);
+    }
+    // steps in fours (one per ring slot; the score buffers swap roles
+    // without a copy); the last round's iterations past the keys only keep
+    // the ring turning in step
+    const int nst = W.nst;
+    for (int x = 0; x < nst; x += 4) {
+        W.template iter<0>(x, SA, SB);
+        W.template iter<1>(x + 1, SB, SA);
+        W.template iter<2>(x + 2, SA, SB);
+        W.template iter<3>(x + 3, SB, SA);
+    }
+    // every wave's outstanding ring loads land before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 
     if (W.bad) s_bad = 1;
     __syncthreads();
@@ -749,7 +862,9 @@ extern "C" pa_status pa_prefill(const void* q, const void* k_cache, const void* 
     if ((int64_t)a.n_tiles * a.ks.P > 65535) return PA_ERR_UNSUPPORTED;
     const int cols = qt_used * G;
     hipError_t e;
-    if (dtype == PA_BF16 && a.ks.PS == 0 && flash_fits(head_dim, block_size) &&
+    // (the workgroup kernel folds the scale into its exponent argument, which
+    // needs a positive scale; other scales take the query tiles)
+    if (dtype == PA_BF16 && a.ks.PS == 0 && flash_fits(head_dim, block_size) && a.sl2 > 0.0f &&
         (int64_t)max_query_len * G >= (int64_t)kFlashCols * kFlashWaves) {
         // chunks that fill a workgroup's tiles: workgroup tiles sharing each step through LDS
         e = head_dim == 128 ? flash_bs<128>(block_size, a) : flash_bs<64>(block_size, a);

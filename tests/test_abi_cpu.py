@@ -430,6 +430,19 @@ def test_plan_on_the_prefix_sharing_workload():
     assert g == [(8 * i, 8) for i in range(4)] and p == [127] * 32 and mg == 8 and mp == 127
 
 
+def test_plan_check_enforces_one_group_per_shared_request():
+    ok = pa.SharedPrefixPlan(np.array([[0, 3], [5, 2]], np.int32), np.array([4, 4, 4, 0, 0, 2, 2], np.int32), 3, 4)
+    ok.check()
+    # a prefix above the bound is allowed (its row is NaN), and so is a request in no group with 0
+    pa.SharedPrefixPlan(ok.groups, np.array([4, 9, 4, 0, 0, 2, 2], np.int32), 3, 4).check()
+    with pytest.raises(ValueError, match="overlaps"):
+        pa.SharedPrefixPlan(np.array([[0, 3], [2, 2]], np.int32), ok.prefix_blocks, 3, 4).check()
+    with pytest.raises(ValueError, match="outside"):
+        pa.SharedPrefixPlan(np.array([[6, 2]], np.int32), ok.prefix_blocks, 3, 4).check()
+    with pytest.raises(ValueError, match="no group"):
+        pa.SharedPrefixPlan(ok.groups, np.array([4, 4, 4, 1, 0, 2, 2], np.int32), 3, 4).check()
+
+
 @pytest.mark.host_lib
 def test_plan_rejects_bad_arguments():
     t = np.zeros((2, 3), np.int32)

@@ -72,6 +72,10 @@ CASES = [
                              block_size=8), (64,)),  # groups of 4: 32 columns at most in float32, head dim 128
     ("f32-G4-D64-bs32", dict(prompts=2, samples=16, prompt_len=170, tail_max=25, dtype="f32", num_q_heads=32,
                              head_dim=64, block_size=32), (64,)),  # 16 x 4 = 64 columns
+    # group sizes that do not divide 16 (a group's columns span tiles unevenly)
+    ("bf16-G3", dict(prompts=2, samples=8, prompt_len=300, tail_max=70, num_q_heads=24), (64, 512)),
+    ("bf16-G5", dict(prompts=3, samples=7, prompt_len=210, tail_max=40, num_q_heads=40), (128,)),
+    ("bf16-G6", dict(prompts=2, samples=9, prompt_len=290, tail_max=33, num_q_heads=48), (64,)),
     # a large batch: 1040 requests in 65 groups of 16
     ("bf16-1040-requests", dict(prompts=65, samples=16, prompt_len=40, tail_max=20), (64,)),
 ]
