@@ -348,6 +348,19 @@ __device__ __forceinline__ void flash_read_values(u32x4 (&v)[D / 16], const char
     }
 }
 
+// Maximum of non-NaN floats as one v_max_f32 / v_max3_f32 (the compiler's
+// fmaxf would canonicalise each operand first).  Vector ALU only.
+__device__ __forceinline__ float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Step token held in element e (scores and value operand) of lane group j.
 template <int BS>
 __device__ __forceinline__ int flash_tok(int tok0, int j, int e) {
@@ -372,36 +385,67 @@ __device__ __forceinline__ void flash_scores(f32x4& sa, f32x4& sb, const u32x4 (
     }
 }
 
-// Online-softmax update and PV of one tile from its step scores, as
-// compute_step does (base 2, lazy rescale), with the scale folded into the
-// exponent argument (scale_log2 > 0) and the causal mask per lane column
+// Online-softmax state of one tile for the workgroup kernel: the running
+// reference m (base 2, scaled), the lane's share of the softmax sum (its
+// own keys' probabilities; the column's total is the sum over its four
+// lanes, taken once at the end: a rescale multiplies every share by the
+// same factor), the accumulators, and two values cached from m: thr, the
+// unscaled score above which a probability could exceed 2^kLazyRescale
+// (thr = (m + kLazyRescale) / scale_log2), and negm = -m (0 while m = -inf).
+template <int D>
+struct FlashState {
+    float m, l, thr, negm;
+    f32x4 acc[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void flash_state_init(FlashState<D>& S) {
+    S.m = -INFINITY;
+    S.l = 0.0f;
+    S.thr = -INFINITY;
+    S.negm = 0.0f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) S.acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Online-softmax update and PV of one tile from its step scores: the
+// method of compute_step (base 2, lazy rescale), with the scale folded into
+// the exponent argument (scale_log2 > 0), the causal mask per lane column
 // (limit Lcol) on a tail step (tail: some column's limit falls inside the
-// step, a wave-uniform test).  v: the step's values, already zeroed at or
-// past the keys' end.
+// step, a wave-uniform test), and the reference moved only when some lane
+// holds a score above its column's cached threshold (a ballot): most steps
+// take no cross-lane maximum and no cross-lane sum.  v: the step's values,
+// already zeroed at or past the keys' end.
 template <int D, int BS>
-__device__ __forceinline__ void flash_softmax_pv(RunState<true, D, BS>& S, f32x4 sa, f32x4 sb,
-                                                 const u32x4 (&v)[D / 16], int tok0, int j, float sl2, int Lcol,
-                                                 bool tail) {
+__device__ __forceinline__ void flash_softmax_pv(FlashState<D>& S, f32x4 sa, f32x4 sb, const u32x4 (&v)[D / 16],
+                                                 int tok0, int j, float sl2, int Lcol, bool tail) {
     float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
     if (tail) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] = flash_tok<BS>(tok0, j, e) < Lcol ? s[e] : -INFINITY;
     }
-    float mx = s[0];
+    // the lane's largest score (scores are never NaN here, so plain v_max3 /
+    // v_max do; fmaxf would add canonicalising instructions)
+    const float lm = vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), vmax(s[6], s[7]));
+    if (__builtin_amdgcn_ballot_w64(lm > S.thr)) {
+        // the column maximum over its four lanes, then the rescale
+        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+        float mx = vmax(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = vmax(__uint_as_float(r32[0]), __uint_as_float(r32[1])) * sl2;
+        const float m_new = vmax(S.m, mx);  // -inf stays -inf (a column with no visible key yet)
+        const float alpha = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(S.m - m_new);
+        S.l *= alpha;
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-    mx = wave_max16(mx) * sl2;
-    rescale<D / 16>(S.m, S.l, S.acc, mx);
-    // a column with no visible key yet keeps m = -inf and gets p = 0
-    const float mref = S.m == -INFINITY ? 0.0f : S.m;
-    float pe[8];
-    float rs = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, -mref));
-        rs += pe[e];
+        for (int c = 0; c < D / 16; ++c) S.acc[c] *= alpha;
+        S.m = m_new;
+        S.thr = (m_new + kLazyRescale) / sl2;
+        S.negm = m_new == -INFINITY ? 0.0f : -m_new;
     }
-    S.l += wave_sum16(rs);
+    float pe[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, S.negm));
+    S.l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
     const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]), pack_bf16x2(pe[4], pe[5]),
                       pack_bf16x2(pe[6], pe[7])};
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
@@ -428,10 +472,10 @@ struct FlashWave {
     FlashOffsets<D, BS, F::TSTRIDE> off;
     int num_blocks, lastb, nst, kend, w, lane, n, j;
     float sl2;
-    bool bad;
+    int bad;  // a table entry outside the pool was met (wave-uniform)
     int Lcol[NCT], Lmin[NCT];
     u32x4 qr[NCT][C::NKC];
-    RunState<true, D, BS> S[NCT];
+    FlashState<D> S[NCT];
 
     template <int SL>
     __device__ __forceinline__ char* slot_keys() {
@@ -449,15 +493,17 @@ struct FlashWave {
     template <int SL>
     __device__ __forceinline__ void issue(const int32_t (&e)[F::NLD]) {
         char* sk = slot_keys<SL>();
+        const uint32_t lane_off = 16u * (uint32_t)lane;
 #pragma unroll
         for (int i = 0; i < F::NLD; ++i) {
             const bool ok = e[i] >= 0 && e[i] < num_blocks;
-            bad |= !ok;
+            bad = __builtin_amdgcn_readfirstlane(bad | (ok ? 0 : 1));
+            // wave-uniform piece base (scalar registers) + the lane's 16 bytes
             const uint64_t o = (uint64_t)(uint32_t)(ok ? e[i] : 0) * blk_bytes + (uint32_t)F::inner(w, i);
             const int lo = F::blk(w, i) * F::TSTRIDE + F::inner(w, i);
-            __builtin_amdgcn_global_load_lds(kbase + o + 16 * lane,
+            __builtin_amdgcn_global_load_lds((kbase + o) + lane_off,
                                              (__attribute__((address_space(3))) void*)(sk + lo), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vbase + o + 16 * lane,
+            __builtin_amdgcn_global_load_lds((vbase + o) + lane_off,
                                              (__attribute__((address_space(3))) void*)(sk + F::SLOT + lo), 16, 0, 0);
         }
     }
@@ -563,7 +609,7 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
     W.lastb = (kend - 1) / BS;
     W.nst = (kend + 31) / 32;
     W.sl2 = scale_log2;
-    W.bad = false;
+    W.bad = 0;
     if (tid == 0) s_bad = 0;
 
     // this wave's query tokens and columns (padding columns repeat the last
@@ -586,7 +632,7 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
         // test is a scalar branch (a wave past the request's tokens: every
         // step is a tail, each lane masked by its own limit)
         W.Lmin[t] = __builtin_amdgcn_readfirstlane(nqw > 0 ? min(pos0 + (16 * t) / G + 1, kend) : 0);
-        run_init(W.S[t]);
+        flash_state_init(W.S[t]);
     }
 
     // prologue: steps 0 .. 3 into slots 0 .. 3; wait for 0 and 1 (2 and 3
@@ -628,10 +674,11 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
     const bool bad = s_bad != 0;
 #pragma unroll
     for (int t = 0; t < NCT; ++t) {
+        const float l = wave_sum16(W.S[t].l);  // the column's sum over its four lanes
         const int c = 16 * t + W.n;
         if (c < ncol) {
             const int64_t row = (int64_t)(t0 + qw + c / G) * Hq + g * G + c % G;
-            store_row<true, D>(out_, row, W.S[t].acc, bad ? __builtin_nanf("") : 1.0f / W.S[t].l, W.j);
+            store_row<true, D>(out_, row, W.S[t].acc, bad ? __builtin_nanf("") : 1.0f / l, W.j);
         }
     }
 }
