@@ -248,16 +248,15 @@ __global__ __launch_bounds__(1024) void prefill_merge_kernel(const float* __rest
 // matrix-core tiles of (token, head) columns, as in prefill_kernel, and the
 // workgroup walks the keys once for all of them, up to its last token's
 // position.  Every 32-token step of keys and values is copied from the pool
-// into a two-slot LDS ring by all the workgroup's lanes: a lane's 16-byte
-// pieces of a step are loaded two steps ahead into registers (the
-// block-table entries they need one load earlier still, so waiting for an
-// entry never waits for the step just issued) and written to the ring one
-// step ahead; the waves read their operands from the ring in the order
-// prefill_kernel reads them from the pool.  One barrier per step separates
-// the writes into a slot from the reads of the step before.  A step's keys
-// and values are read from the pool once per workgroup instead of once per
-// wave, and two waves fit a SIMD (at most 256 registers each), so one
-// wave's softmax work overlaps the other's matrix-core work.
+// into a four-slot LDS ring by direct global-to-LDS loads (no staging
+// registers), each wave moving its own 1 KiB pieces, four steps ahead of
+// the step whose slot they refill; the waves read their operands from the
+// ring in the order prefill_kernel reads them from the pool.  One barrier
+// per step makes the step two ahead visible and frees the slot just read.
+// A step's keys and values are read from the pool once per workgroup
+// instead of once per wave, and two workgroups fit a CU (two waves per
+// SIMD, at most 256 registers each), so one wave's softmax work overlaps
+// the other's matrix-core work.
 
 // s_waitcnt immediate (gfx9 encoding) that waits for at most n outstanding
 // vector-memory loads and leaves the export and LDS/scalar counters alone.
