@@ -48,6 +48,11 @@
  * 3 of o (0-3, 8-11, 4-7, 12-15 within each 16 offsets): the 8 values a
  * matrix-core lane needs are then one 16-byte load.  A (block, head) tile is
  * contiguous (block_size * head_dim elements for each of K and V).
+ * Pools are written only through this library (pa_cache_write,
+ * pa_decode_append, pa_decode_append_noalloc, pa_copy_blocks,
+ * pa_swap_blocks), which store in this order; a pool filled any other way
+ * must follow the formulas above exactly, or attention reads other values
+ * than the caller meant (no check can tell).
  */
 #ifndef PA_H
 #define PA_H
