@@ -258,6 +258,10 @@ __global__ __launch_bounds__(1024) void prefill_merge_kernel(const float* __rest
 // SIMD, at most 256 registers each), so one wave's softmax work overlaps
 // the other's matrix-core work.
 
+// Largest batch whose workgroups are dispatched longest request first (at
+// most one request per lane of a workgroup).
+constexpr int kFlashOrderMax = 256;
+
 // s_waitcnt immediate (gfx9 encoding) that waits for at most n outstanding
 // vector-memory loads and leaves the export and LDS/scalar counters alone.
 constexpr int vmcnt_only(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
@@ -565,15 +569,58 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
     __shared__ __attribute__((aligned(16))) char ring2[2 * F::SLOT];
     __shared__ __attribute__((aligned(16))) char ring3[2 * F::SLOT];
     __shared__ int s_bad;
+    __shared__ int s_len[kFlashOrderMax];
+    __shared__ int s_req, s_t0, s_t1;
     const int g = blockIdx.x;
     const int qt = blockIdx.y;
-    const int b = blockIdx.z;
     const int tid = threadIdx.x;
-    const int t0 = q_start[b];
-    const int t1 = q_start[b + 1];
+    // Longest requests first: a workgroup walks its request's keys, so with
+    // more workgroups than the CUs hold at once, a long request dispatched
+    // last sets the end.  Workgroups are dispatched in index order, so
+    // blockIdx.z is taken as a rank in length order (longest first, ties in
+    // index order) for batches of up to kFlashOrderMax requests; each
+    // workgroup finds the request of its rank (a strict order: exactly one
+    // request has it).  Larger batches keep the index order.
+    static_assert(kFlashOrderMax <= 64 * NW, "one request per lane");
+    int b = blockIdx.z;
+    int t0, t1, L;
+    const int B = (int)gridDim.z;
+    if (B <= kFlashOrderMax) {
+        // one round trip: every request's length and query offsets at once
+        int my_t0 = 0, my_t1 = 0;
+        if (tid < B) {
+            s_len[tid] = lens[tid];
+            my_t0 = q_start[tid];
+            my_t1 = q_start[tid + 1];
+        }
+        __syncthreads();
+        if (tid < B) {
+            const int lt = s_len[tid];
+            int rank = 0;
+            for (int u = 0; u < B; ++u) {
+                const int lu = s_len[u];
+                rank += (lu > lt || (lu == lt && u < tid)) ? 1 : 0;
+            }
+            if (rank == b) {
+                s_req = tid;
+                s_t0 = my_t0;
+                s_t1 = my_t1;
+            }
+        }
+        __syncthreads();
+        // wave-uniform (the same LDS words for every lane): the table row and
+        // the entry loads stay scalar
+        b = __builtin_amdgcn_readfirstlane(s_req);
+        t0 = __builtin_amdgcn_readfirstlane(s_t0);
+        t1 = __builtin_amdgcn_readfirstlane(s_t1);
+        L = __builtin_amdgcn_readfirstlane(s_len[b]);
+    } else {
+        t0 = q_start[b];
+        t1 = q_start[b + 1];
+        L = lens[b];
+    }
     if (t0 < 0 || t1 > T || t1 < t0) return;  // malformed query offsets: the request writes nothing
     const int M = t1 - t0;
-    const int L = lens[b];
     if (M > max_q || M > L || (int64_t)L > (int64_t)max_blocks * BS) {
         // as prefill_kernel: the first tile writes NaN in all the request's rows
         if (qt != 0) return;
