@@ -210,6 +210,30 @@ def test_workgroup_tiles_error_rows_without_fault(bs, hq, d):
     assert np.abs(got[keep] - ref[keep]).max() <= 2e-2
 
 
+@pytest.mark.parametrize("label,lens,m", [
+    # more requests than the workgroup kernel orders by length: index order
+    ("300-requests", [40 + (37 * i) % 260 for i in range(300)], 40),
+    # equal lengths (ties go in index order) with a few longer ones
+    ("ties", [200] * 9 + [330, 200, 330], 64),
+])
+def test_workgroup_tiles_request_order(label, lens, m):
+    """The workgroup kernel takes its request by length rank for batches of
+    up to 256 requests and by index beyond: every row right either way."""
+    w = custom(seed=61 + len(lens), dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+               lens=lens)
+    pool, _, tables, _, _ = replay(w)
+    dev = build_device_batch(w)
+    dev.cache_append()
+    mq = np.minimum(w.seq_lens, m)
+    assert pa.prefill_path(w.batch, 32, 8, int(mq.max()), 0, head_dim=128, block_size=16) == "workgroup tiles"
+    q, qs, got = run(w, dev, mq, balanced=False)
+    ref = oa.paged_prefill(q, pool.k, pool.v, tables, w.seq_lens, qs, w.scale)
+    err = float(np.abs(got - ref).max())
+    say("request order", label, "B", w.batch, "max abs err", f"{err:.3e}")
+    assert not np.isnan(got).any()
+    assert err <= 2e-2
+
+
 def test_balanced_verify_error_rows_and_workspace_reuse():
     """The balanced path: NaN rows for impossible requests, zero-length chunks, counters left at zero."""
     w = custom(seed=21, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
