@@ -480,8 +480,22 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str,
         del scratch
         return t
 
+    def time_decode_single(n):
+        # hot launches timed like the cold ones, one event pair each: the
+        # difference to the back-to-back time is what a per-launch event pair
+        # adds (the wait between the first event and the kernel's start)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            attend()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
     hot = np.array([time_decode_hot(max(steps, 20)) for _ in range(3)])
     cold = time_decode_cold(cold_iters)
+    single = time_decode_single(cold_iters)
 
     # calibration: a plain streaming read of the same byte count
     import paged_kv_cache_348_amd as pa
@@ -540,7 +554,8 @@ def gpu_bench(w, steps: int, warmup: int, partition_size: int, decode_mode: str,
     ca1.record(stream)
     torch.cuda.synchronize()
     ms_append = ca0.elapsed_time(ca1) / steps
-    return dict(ms_step=ms_step, wall_s=t_wall, hot_ms=hot, cold_ms=cold, ms_append=ms_append, out=out,
+    return dict(ms_step=ms_step, wall_s=t_wall, hot_ms=hot, cold_ms=cold, single_ms=single, ms_append=ms_append,
+                out=out,
                 stream_read_gbps=nbytes / (sr_ms * 1e-3) / 1e9,
                 device=dev_name, width=dev.max_blocks, launches=dev.launches,
                 read_bytes=read_bytes, algo_bytes=algo_bytes, swap_ms=swap, swap_bytes=swap_bytes, swap_blocks=nsw)
@@ -657,6 +672,8 @@ def main(argv=None):
     t_launch = ms * 1e-3 if fused else t_dec
     achieved = algo_bytes / t_launch / 1e9
     t_cold = float(np.median(cold)) * 1e-3
+    # per-launch event gap, measured on hot launches in this run
+    gap = max(0.0, float(np.median(g["single_ms"])) - float(np.median(hot))) * 1e-3
     err = None
     if ref is not None:
         err = float(np.abs(g["out"] - ref).max())
@@ -698,7 +715,9 @@ def main(argv=None):
         "kv_unique_read_bytes": read_bytes,
         "kv_read_frac_of_8tbs_step": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "decode_us": {"hot": float(np.median(hot)) * 1e3, "hot_runs": [float(x) * 1e3 for x in hot],
-                      "cold_median": float(np.median(cold)) * 1e3, "cold_min": float(cold.min()) * 1e3},
+                      "cold_median": float(np.median(cold)) * 1e3, "cold_min": float(cold.min()) * 1e3,
+                      "hot_one_event_pair_each": float(np.median(g["single_ms"])) * 1e3,
+                      "event_pair_gap": gap * 1e6},
         "cache_append_us": g["ms_append"] * 1e3,
         "swap": {  # pa_swap_blocks to / from a pinned host pool (host link: PCIe 5.0 x16, 64 GB/s each way)
             "blocks": g["swap_blocks"], "bytes": g["swap_bytes"],
@@ -721,6 +740,10 @@ def main(argv=None):
             # pair per launch, median of the launches
             "achieved_cold": algo_bytes / t_cold / 1e9,
             "frac_cold": algo_bytes / t_cold / 1e9 / HBM_PEAK_GBPS,
+            # the same cold median less the event-pair gap measured on hot
+            # launches timed the same way (a kernel trace of cold launches,
+            # bench.py --cold-only, times the kernel with no events at all)
+            "frac_cold_net": algo_bytes / max(t_cold - gap, 1e-9) / 1e9 / HBM_PEAK_GBPS,
             "traffic": (measured_traffic(args.workload, mode, fused)
                         if ps == DEFAULT_PARTITION.get(args.workload, ps)
                         and mode == DEFAULT_DECODE.get(args.workload, "split") else None),
