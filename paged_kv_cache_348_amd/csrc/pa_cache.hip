@@ -58,8 +58,9 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict
 // BS - 1 tokens past it), and every token of the window that belongs to no
 // full block (written one token at a time, as above).  A token of a full
 // block whose first token lies in an earlier window is that window's.
-// Rows are staged through LDS with coalesced 16-byte loads; the LDS row
-// stride has 16 bytes of padding, so the tile-order reads of 16 lanes (one
+// The slots and every row the workgroup may write are loaded in one round
+// trip (all loads in flight at once) and the rows staged through LDS; the
+// LDS row stride has 16 bytes of padding, so the tile-order reads of 16 lanes (one
 // token each) fall in different banks.
 template <int ES, int D, int BS>
 struct BulkCfg {
@@ -85,10 +86,9 @@ __global__ __launch_bounds__(256) void cache_write_bulk_kernel(const char* __res
     __shared__ __align__(16) char lk[C::ROWS * C::RS];
     __shared__ __align__(16) char lv[C::ROWS * C::RS];
     __shared__ int64_t ls[C::NS];
-    __shared__ uint8_t need[C::ROWS];  // row r (token t0 + r) is read by this workgroup
     __shared__ int lead[C::W / BS];    // window positions of the full blocks it owns
     __shared__ int scat[C::W];         // window positions of its single tokens
-    __shared__ int n_lead, n_scat, n_rows;
+    __shared__ int n_lead, n_scat;
     const int tid = threadIdx.x;
     const int h = blockIdx.y;
     const int64_t t0 = (int64_t)blockIdx.x * C::W;
@@ -96,14 +96,40 @@ __global__ __launch_bounds__(256) void cache_write_bulk_kernel(const char* __res
     if (tid == 0) {
         n_lead = 0;
         n_scat = 0;
-        n_rows = 0;
     }
-    for (int i = tid; i < C::NS; i += 256) {
-        const int64_t t = t0 - (BS - 1) + i;
-        const int64_t sl = (t >= 0 && t < T) ? slots[t] : -1;
-        ls[i] = (sl >= 0 && sl < total_slots) ? sl : -1;
+    // one round trip: the window's slots (with the BS - 1 before and after it)
+    // and every row the workgroup may write, its window's and the BS - 1
+    // after it where a full block starting in the window can end (those are
+    // the next workgroup's first rows, read at about the same time)
+    static_assert(C::NS <= 256, "one slot per lane");
+    int64_t my_sl = -1;
+    if (tid < C::NS) {
+        const int64_t t = t0 - (BS - 1) + tid;
+        if (t >= 0 && t < T) my_sl = slots[t];
     }
-    for (int r = tid; r < C::ROWS; r += 256) need[r] = 0;
+    {
+        constexpr int NP = (C::ROWS * C::CH + 255) / 256;  // 16-byte pieces per lane
+        u32x4 kr[NP], vr[NP];
+        // every load in flight at once, none under a branch: the piece index
+        // is clamped to the last piece (a repeat of its load and LDS write)
+        // and the row to the last token (rows past it are never read)
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int p = min(tid + 256 * i, C::ROWS * C::CH - 1);
+            const int r = p / C::CH, c = p % C::CH;
+            const int64_t src = (min(t0 + r, T - 1) * Hkv + h) * (int64_t)C::ROW + c * 16;
+            kr[i] = ld16(k + src);
+            vr[i] = ld16(v + src);
+        }
+        if (tid < C::NS) ls[tid] = (my_sl >= 0 && my_sl < total_slots) ? my_sl : -1;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int p = min(tid + 256 * i, C::ROWS * C::CH - 1);
+            const int r = p / C::CH, c = p % C::CH;
+            *reinterpret_cast<u32x4*>(lk + r * C::RS + c * 16) = kr[i];
+            *reinterpret_cast<u32x4*>(lv + r * C::RS + c * 16) = vr[i];
+        }
+    }
     __syncthreads();
 
     // slot index i = window position + BS - 1; a full block starts there when
@@ -121,30 +147,11 @@ __global__ __launch_bounds__(256) void cache_write_bulk_kernel(const char* __res
         if (s >= 0) {
             const int off = (int)(s % BS);
             if (full_from(tid - off + BS - 1)) {  // in a full block
-                if (off == 0) {                   // ... whose first token is this one: owned here
-                    lead[atomicAdd(&n_lead, 1)] = tid;
-                    atomicMax(&n_rows, tid + BS);
-                    for (int q = 0; q < BS; ++q) need[tid + q] = 1;
-                }
+                if (off == 0) lead[atomicAdd(&n_lead, 1)] = tid;  // ... whose first token is this one: owned here
             } else {
                 scat[atomicAdd(&n_scat, 1)] = tid;
-                atomicMax(&n_rows, tid + 1);
-                need[tid] = 1;
             }
         }
-    }
-    __syncthreads();
-
-    // stage the rows this workgroup writes (keys and values of head h)
-    const int rows = n_rows;
-    for (int p = tid; p < rows * C::CH; p += 256) {
-        const int r = p / C::CH, c = p % C::CH;
-        if (!need[r]) continue;
-        const int64_t src = ((t0 + r) * Hkv + h) * (int64_t)C::ROW + c * 16;
-        const u32x4 kv = ld16(k + src);
-        const u32x4 vv = ld16(v + src);
-        *reinterpret_cast<u32x4*>(lk + r * C::RS + c * 16) = kv;
-        *reinterpret_cast<u32x4*>(lv + r * C::RS + c * 16) = vv;
     }
     __syncthreads();
 
