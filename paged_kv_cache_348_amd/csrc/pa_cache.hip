@@ -90,8 +90,13 @@ __global__ __launch_bounds__(256) void cache_write_bulk_kernel(const char* __res
     __shared__ int scat[C::W];         // window positions of its single tokens
     __shared__ int n_lead, n_scat;
     const int tid = threadIdx.x;
-    const int h = blockIdx.y;
-    const int64_t t0 = (int64_t)blockIdx.x * C::W;
+    // workgroup id = window * Hkv + kv-head: consecutive windows of one head
+    // are Hkv ids apart, so with the ids dealt round-robin over the XCDs they
+    // share an XCD (and its L2) whenever Hkv is a multiple of the XCD count,
+    // and the BS - 1 rows a workgroup reads past its window are read from L2
+    // by the next one
+    const int h = (int)(blockIdx.x % (unsigned)Hkv);
+    const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)Hkv) * C::W;
 
     if (tid == 0) {
         n_lead = 0;
@@ -277,7 +282,9 @@ template <int ES, int D, int BS>
 pa_status launch_bulk_t(const char* kp, const char* vp, const int64_t* slots, char* kcp, char* vcp, int64_t T,
                         int Hkv, int64_t total_slots, hipStream_t s) {
     using C = pa::BulkCfg<ES, D, BS>;
-    const dim3 grid((unsigned)((T + C::W - 1) / C::W), (unsigned)Hkv);
+    const int64_t nwg = ((T + C::W - 1) / C::W) * Hkv;  // (window, kv-head) workgroups
+    if (nwg > 2147483647LL) return PA_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)nwg);
     hipLaunchKernelGGL((pa::cache_write_bulk_kernel<ES, D, BS>), grid, dim3(256), 0, s, kp, vp, slots, kcp, vcp, T, Hkv,
                        total_slots);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -327,7 +334,6 @@ extern "C" pa_status pa_cache_write(const void* k, const void* v, const int64_t*
     // decode-sized appends (about one token per block) store non-temporally,
     // one thread per 16-byte chunk; bulk appends write whole tiles
     if (num_tokens > kNonTemporalMaxTokens) {
-        if ((int64_t)num_tokens / 16 + 1 > 2147483647LL || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
         return launch_bulk(dtype, head_dim, block_size, kp, vp, slot_mapping, kcp, vcp, num_tokens, num_kv_heads,
                            total_slots, s);
     }
