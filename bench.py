@@ -47,7 +47,7 @@ PARTITION_BALANCED = -1  # the library's balanced split (PA_PARTITION_BALANCED)
 # log-sum-exp merge; with prefix sharing, fixed partitions dispatch the
 # samples of one prompt together, so their shared blocks are read while
 # still in L2 / MALL)
-DEFAULT_PARTITION = {"llama3_8b": PARTITION_BALANCED, "llama_70b": PARTITION_BALANCED, "prefix_share": 512}
+DEFAULT_PARTITION = {"llama3_8b": PARTITION_BALANCED, "llama_70b": PARTITION_BALANCED, "prefix_share": 1024}
 # decode entry point per workload: with prefix sharing, the shared-prefix
 # decode reads each prompt's blocks once for all of its samples
 DEFAULT_DECODE = {"prefix_share": "shared"}

@@ -212,19 +212,6 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
     return v;
 }
 
-// Two floats written / read as one 64-bit agent-scope atomic access: the
-// access goes to the device-coherent level, so a wave on another XCD that
-// reads it after a later counter update sees it.
-__device__ __forceinline__ void coherent_store(uint64_t* p, float lo, float hi) {
-    const uint64_t v = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float2 coherent_load(const uint64_t* p) {
-    const uint64_t v = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-
 // Wave-uniform copies (values read from LDS land in vector registers; the
 // loop state derived from them is kept in scalar registers this way).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "pa_device.h"
 
@@ -149,6 +150,19 @@ __device__ __forceinline__ void issue_step_e(StepRegs<BF16, D, BS>& r, const cha
             r.v[c] = ld16_stream(vp + (int64_t)d * BS * C::ES);
         }
     }
+}
+
+// Two floats written / read as one 64-bit agent-scope atomic access: the
+// access goes to the device-coherent level, so a wave on another XCD that
+// reads it after a later counter update sees it.
+__device__ __forceinline__ void coherent_store(uint64_t* p, float lo, float hi) {
+    const uint64_t v = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 coherent_load(const uint64_t* p) {
+    const uint64_t v = __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
 // Reductions over the four lanes l, l^16, l^32, l^48 (one head column).
@@ -360,41 +374,67 @@ __device__ __forceinline__ void load_q(typename DecodeCfg<BF16, D, BS>::QRegs& q
     for (int c = 0; c < C::NKC; ++c) qr[c] = (n < G) ? ld16(qp + (int64_t)(4 * c + j) * 16) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Attention over tokens [start, end) of one sequence (0 <= start < end <= L)
-// for one kv-head: the block table is walked in chunks of kTableChunk
-// entries (one per lane, read back with readlane), and inside a chunk the
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+// Attention over tokens [ctok, cend) of one sequence (cend - ctok <=
+// kTableChunk * BS, cend <= L) for one kv-head: the chunk's block-table
+// entries are read once (one per lane, read back with readlane) and the
 // tokens are streamed in steps through a two-stage load pipeline.  The loop
 // body issues the next step's loads unconditionally, so the wait before each
-// compute covers only the current step's loads.
+// compute covers only the current step's loads.  hook() runs after the
+// table entries have arrived and before the first step's loads are issued:
+// work on loads the caller issued before the call costs no round trip of
+// its own there.  Returns false (S.bad set, nothing read) on an entry
+// outside the pool.
+template <bool BF16, int D, int BS, class Hook = NoHook>
+__device__ __forceinline__ bool attend_chunk(RunState<BF16, D, BS>& S,
+                                             const u32x4 (&qr)[DecodeCfg<BF16, D, BS>::NKC],
+                                             const char* __restrict__ kbase, const char* __restrict__ vbase,
+                                             int64_t blk_bytes, const int32_t* __restrict__ trow, int num_blocks,
+                                             int ctok, int cend, int L, int lane, int n, int j, float scale_log2,
+                                             Hook&& hook = Hook{}) {
+    using C = DecodeCfg<BF16, D, BS>;
+    const int blk0 = ctok / BS;
+    const int nblk = (cend - 1) / BS - blk0 + 1;
+    const int32_t ent = (lane < nblk) ? trow[blk0 + lane] : 0;
+    const bool bad = __any(lane < nblk && (ent < 0 || ent >= num_blocks));
+    if constexpr (!std::is_same_v<std::decay_t<Hook>, NoHook>) {
+        hook();
+        __builtin_amdgcn_sched_barrier(0);  // the hook's registers die before the first step's are allocated
+    }
+    if (bad) {
+        S.bad = true;
+        return false;
+    }
+    const int nst = (cend - ctok + C::STEP - 1) / C::STEP;
+    StepRegs<BF16, D, BS> cur;
+    issue_step<BF16, D, BS>(cur, kbase, vbase, blk_bytes, ent, blk0, nblk, ctok, L, n, j);
+    int tok0 = ctok;
+    for (int st = 0; st + 1 < nst; ++st, tok0 += C::STEP) {
+        StepRegs<BF16, D, BS> nxt;
+        issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, L, n, j);
+        __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the compute
+        compute_step<BF16, D, BS>(cur, qr, S.m, S.l, S.acc, tok0, L, j, scale_log2);
+        cur = nxt;
+    }
+    compute_step<BF16, D, BS>(cur, qr, S.m, S.l, S.acc, tok0, L, j, scale_log2);
+    return true;
+}
+
+// Attention over tokens [start, end) of one sequence (0 <= start < end <= L)
+// for one kv-head, walking the block table in chunks of kTableChunk entries.
 template <bool BF16, int D, int BS>
 __device__ __forceinline__ void attend_range(RunState<BF16, D, BS>& S,
                                              const u32x4 (&qr)[DecodeCfg<BF16, D, BS>::NKC],
                                              const char* __restrict__ kbase, const char* __restrict__ vbase,
                                              int64_t blk_bytes, const int32_t* __restrict__ trow, int num_blocks,
                                              int start, int end, int L, int lane, int n, int j, float scale_log2) {
-    using C = DecodeCfg<BF16, D, BS>;
-    for (int ctok = start; ctok < end; ctok += kTableChunk * BS) {
-        const int cend = min(ctok + kTableChunk * BS, end);
-        const int blk0 = ctok / BS;
-        const int nblk = (cend - 1) / BS - blk0 + 1;
-        const int32_t ent = (lane < nblk) ? trow[blk0 + lane] : 0;
-        if (__any(lane < nblk && (ent < 0 || ent >= num_blocks))) {
-            S.bad = true;
+    for (int ctok = start; ctok < end; ctok += kTableChunk * BS)
+        if (!attend_chunk<BF16, D, BS>(S, qr, kbase, vbase, blk_bytes, trow, num_blocks, ctok,
+                                       min(ctok + kTableChunk * BS, end), L, lane, n, j, scale_log2))
             return;
-        }
-        const int nst = (cend - ctok + C::STEP - 1) / C::STEP;
-        StepRegs<BF16, D, BS> cur;
-        issue_step<BF16, D, BS>(cur, kbase, vbase, blk_bytes, ent, blk0, nblk, ctok, L, n, j);
-        int tok0 = ctok;
-        for (int st = 0; st + 1 < nst; ++st, tok0 += C::STEP) {
-            StepRegs<BF16, D, BS> nxt;
-            issue_step<BF16, D, BS>(nxt, kbase, vbase, blk_bytes, ent, blk0, nblk, tok0 + C::STEP, L, n, j);
-            __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the compute
-            compute_step<BF16, D, BS>(cur, qr, S.m, S.l, S.acc, tok0, L, j, scale_log2);
-            cur = nxt;
-        }
-        compute_step<BF16, D, BS>(cur, qr, S.m, S.l, S.acc, tok0, L, j, scale_log2);
-    }
 }
 
 // Normalise and store the G output rows of one (sequence, kv-head) starting

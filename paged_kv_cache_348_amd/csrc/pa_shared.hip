@@ -7,7 +7,7 @@
 // shared blocks allow is reading each shared key/value tile once for all the
 // requests of a group instead of once per request.
 //
-// Three kernels:
+// Two kernels:
 //  - decode_prefix_kernel: one wave per (kv-head, partition of the shared
 //    prefix, group).  The group's queries for that kv-head (group size x G
 //    columns, up to 64, in 16-column matrix-core tiles) all attend over the
@@ -15,9 +15,15 @@
 //    every column tile.  Each (request, head) gets a partial (o, m, l).
 //  - decode_suffix_kernel: one wave per (kv-head, partition of the rest,
 //    request): the usual decode over the request's own tokens past the
-//    prefix, leaving partials after the prefix ones.
-//  - merge_shared_kernel: log-sum-exp merge of a row's prefix and suffix
-//    partials, M = max_j m_j, w_j = l_j 2^(m_j - M), out = sum w_j o_j / sum w_j.
+//    prefix.  When those fit one partition (the common case for forks),
+//    the wave folds the row's prefix partials into its own state and
+//    writes the output rows.  Otherwise each partition leaves a partial
+//    after the prefix ones and counts itself in; the wave that brings the
+//    (request, kv-head) counter to the partition count merges the prefix
+//    and suffix partials by the log-sum-exp rule,
+//      M = max_j m_j,  w_j = l_j 2^(m_j - M),  out = sum w_j o_j / sum w_j,
+//    and writes the rows.  The counters are cleared by the prefix kernel
+//    (or a fill kernel when there is no prefix work), which runs first.
 // The prefix is cut at a multiple of max(32, block_size) tokens so both
 // parts start on a step and block boundary; the few tokens between that cut
 // and the end of the shared blocks go with the suffix.
@@ -101,8 +107,9 @@ template <bool BF16, int D, int BS, int NCT>
 __global__ __launch_bounds__(64) void decode_prefix_kernel(
     const void* __restrict__ q_, const void* __restrict__ kc_, const void* __restrict__ vc_,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ groups,
-    const int32_t* __restrict__ prefix_blocks, float* __restrict__ part_o, float* __restrict__ part_ml, int B, int Hq,
-    int Hkv, int G, int max_blocks, int max_pre, int num_blocks, int max_group, int PS, int P_max, float scale_log2) {
+    const int32_t* __restrict__ prefix_blocks, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int32_t* __restrict__ counters, int ncounters, int B, int Hq, int Hkv, int G, int max_blocks, int max_pre,
+    int num_blocks, int max_group, int PS, int P_max, float scale_log2) {
     using C = DecodeCfg<BF16, D, BS>;
     const int g = blockIdx.x;
     const int p = blockIdx.y;
@@ -110,11 +117,17 @@ __global__ __launch_bounds__(64) void decode_prefix_kernel(
     const int lane = threadIdx.x;
     const int n = lane & 15;
     const int j = lane >> 4;
+    {
+        // the suffix kernel's merge counters, cleared before it starts
+        const int64_t wid = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+        const int64_t nwv = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+        for (int64_t i = wid * 64 + lane; i < ncounters; i += nwv * 64) counters[i] = 0;
+    }
     const int s0 = groups[2 * gi];
     const int ns = groups[2 * gi + 1];
     if (s0 < 0 || ns < 1 || ns > B - s0) return;  // a malformed group has no prefix work
     const int pb = prefix_blocks[s0];
-    if (pb <= 0 || pb > max_pre) return;  // the suffix or merge kernel handles such rows
+    if (pb <= 0 || pb > max_pre) return;  // the suffix kernel handles such rows
     const int T = shared_tokens<BS>(pb);
     const int start = p * PS;
     if (start >= T) return;
@@ -156,12 +169,85 @@ __global__ __launch_bounds__(64) void decode_prefix_kernel(
     }
 }
 
+// Folding a row's partials (normalised o, m, l) into a running state S by
+// the log-sum-exp rule, NU partials at a time: load() issues one batch's
+// loads, add() folds the batch in.  Lane (n, j) holds its column's
+// accumulator rows 16c + 4j ...
+template <bool BF16, int D, int BS, int NU>
+struct PartialBatch {
+    float m[NU], l[NU];
+    f32x4 o[NU][DecodeCfg<BF16, D, BS>::NV];
+
+    __device__ __forceinline__ void load(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                         int64_t base, int i0, int npre, int j) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int64_t pr = base + min(i0 + u, npre - 1);  // past the end: a valid partial, skipped in add()
+            m[u] = part_ml[2 * pr];
+            l[u] = part_ml[2 * pr + 1];
+#pragma unroll
+            for (int c = 0; c < DecodeCfg<BF16, D, BS>::NV; ++c)
+                o[u][c] = *reinterpret_cast<const f32x4*>(part_o + pr * D + 16 * c + 4 * j);
+        }
+    }
+
+    __device__ __forceinline__ void add(RunState<BF16, D, BS>& S, int count) const {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if (u >= count) break;
+            const float M = fmaxf(S.m, m[u]);
+            const float a = S.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(S.m - M);
+            const float w = l[u] * __builtin_amdgcn_exp2f(m[u] - M);
+            S.l = S.l * a + w;
+#pragma unroll
+            for (int c = 0; c < DecodeCfg<BF16, D, BS>::NV; ++c) S.acc[c] = S.acc[c] * a + o[u][c] * w;
+            S.m = M;
+        }
+    }
+};
+
+// Merge of output rows row0 .. row0 + G - 1 from their prefix partials
+// [0, npre) and suffix partials [P_pre, P_pre + nsuf) (log-sum-exp rule),
+// written by other waves of this launch or by the prefix kernel, read at the
+// device-coherent level.
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void merge_row_partials(const float* __restrict__ part_o,
+                                                   const float* __restrict__ part_ml, void* __restrict__ out_,
+                                                   int64_t row0, int P_max, int npre, int P_pre, int nsuf, int n,
+                                                   int j, int G) {
+    using C = DecodeCfg<BF16, D, BS>;
+    if (n >= G) return;
+    const int64_t rbase = (row0 + n) * P_max;
+    auto slot = [&](int i) { return rbase + (i < npre ? i : P_pre + (i - npre)); };
+    const int np = npre + nsuf;
+    float M = -INFINITY;
+    for (int i = 0; i < np; ++i)
+        M = fmaxf(M, coherent_load(reinterpret_cast<const uint64_t*>(part_ml + 2 * slot(i))).x);
+    RunState<BF16, D, BS> Mg;
+    run_init(Mg);
+    Mg.m = M;
+    for (int i = 0; i < np; ++i) {
+        const float2 ml = coherent_load(reinterpret_cast<const uint64_t*>(part_ml + 2 * slot(i)));
+        const float wt = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
+        Mg.l += wt;
+        const uint64_t* po = reinterpret_cast<const uint64_t*>(part_o + slot(i) * D);
+#pragma unroll
+        for (int c = 0; c < C::NV; ++c) {
+            const int e = (16 * c + 4 * j) / 2;
+            const float2 lo = coherent_load(po + e), hi = coherent_load(po + e + 1);
+            Mg.acc[c] += wt * f32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+    }
+    store_out<BF16, D, BS>(out_, row0, Mg, n, j, G);
+}
+
 template <bool BF16, int D, int BS>
 __global__ __launch_bounds__(64) void decode_suffix_kernel(
     const void* __restrict__ q_, const void* __restrict__ kc_, const void* __restrict__ vc_,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens, const int32_t* __restrict__ prefix_blocks,
-    float* __restrict__ part_o, float* __restrict__ part_ml, int Hq, int Hkv, int G, int max_blocks, int max_pre,
-    int num_blocks, int PS, int P_pre, int P_max, float scale_log2) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, int32_t* __restrict__ counters, void* __restrict__ out_,
+    int Hq, int Hkv, int G, int max_blocks, int max_pre, int num_blocks, int PS, int P_pre, int P_max,
+    float scale_log2) {
     using C = DecodeCfg<BF16, D, BS>;
     const int g = blockIdx.x;
     const int b = blockIdx.y;
@@ -171,105 +257,86 @@ __global__ __launch_bounds__(64) void decode_suffix_kernel(
     const int j = lane >> 4;
     const int L = lens[b];
     const int pb = prefix_blocks[b];
-    if (L <= 0 || (int64_t)L > (int64_t)max_blocks * BS || pb < 0 || pb > max_pre) return;  // merge writes the row
-    const int T = shared_tokens<BS>(pb);
-    if (T > L) return;
-    const int start = T + p * PS;
-    if (start >= L) return;
-    const int end = min(start + PS, L);
     const int64_t row0 = (int64_t)b * Hq + g * G;
+    if (L <= 0 || (int64_t)L > (int64_t)max_blocks * BS || pb < 0 || pb > max_pre || shared_tokens<BS>(pb) > L) {
+        // empty request: zero rows; a length or prefix the table cannot hold: NaN rows
+        if (p == 0) fill_rows<BF16, D>(out_, row0, G, L <= 0 ? 0.0f : __builtin_nanf(""), lane);
+        return;
+    }
+    const int T = shared_tokens<BS>(pb);
+    const int npre = (T + PS - 1) / PS;
+    const int nsuf = (L - T + PS - 1) / PS;
+    // own tokens in one partition (or none): this wave finishes the rows,
+    // folding the prefix partials into its state
+    const bool single = nsuf <= 1;
+    if (single ? p > 0 : p >= nsuf) return;
+    const int start = T + p * PS;
+    const int end = min(start + PS, L);
     typename C::QRegs qr;
     load_q<BF16, D, BS>(qr, q_, row0 + n, n, j, G);
     RunState<BF16, D, BS> S;
     run_init(S);
     const int64_t blk_bytes = (int64_t)Hkv * C::TILE * C::ES;
-    attend_range<BF16, D, BS>(S, qr, reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES,
-                              reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES, blk_bytes,
-                              tables + (int64_t)b * max_blocks, num_blocks, start, end, L, lane, n, j, scale_log2);
-    if (n < G) store_partial<BF16, D, BS>(part_o, part_ml, row0 + n, P_max, P_pre + p, S, j);
+    const char* kbase = reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES;
+    const char* vbase = reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES;
+    const int32_t* trow = tables + (int64_t)b * max_blocks;
+    if (!single) {
+        attend_chunk<BF16, D, BS>(S, qr, kbase, vbase, blk_bytes, trow, num_blocks, start, end, L, lane, n, j,
+                                  scale_log2);
+        // the partial at the device-coherent level, then the count
+        if (n < G) {
+            const int64_t prow = (row0 + n) * P_max + P_pre + p;
+            const float inv = S.bad ? __builtin_nanf("") : 1.0f / S.l;
+            uint64_t* po = reinterpret_cast<uint64_t*>(part_o + prow * D);
+#pragma unroll
+            for (int c = 0; c < C::NV; ++c) {
+                const int e = (16 * c + 4 * j) / 2;
+                coherent_store(po + e, S.acc[c][0] * inv, S.acc[c][1] * inv);
+                coherent_store(po + e + 1, S.acc[c][2] * inv, S.acc[c][3] * inv);
+            }
+            if (j == 0)
+                coherent_store(reinterpret_cast<uint64_t*>(part_ml + 2 * prow), S.bad ? 0.0f : S.m,
+                               S.bad ? 1.0f : S.l);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before the count
+        int old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(counters + (int64_t)b * Hkv + g, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        old = __shfl(old, 0, 64);
+        if (old == nsuf - 1) merge_row_partials<BF16, D, BS>(part_o, part_ml, out_, row0, P_max, npre, P_pre, nsuf,
+                                                             n, j, G);
+        return;
+    }
+    // The prefix partials start the state: the first batch's loads go out
+    // with the table entries, so they cost no round trip of their own.  The
+    // padding columns n >= G read row G - 1's partials and store nothing.
+    constexpr int NU = 2;  // partials per batch (four would cost a wave per SIMD in float32)
+    const int64_t base = (row0 + min(n, G - 1)) * P_max;
+    PartialBatch<BF16, D, BS, NU> pb0;
+    if (npre > 0) pb0.load(part_o, part_ml, base, 0, npre, j);
+    auto fold = [&]() {
+        if (npre <= 0) return;
+        pb0.add(S, min(npre, NU));
+        for (int i0 = NU; i0 < npre; i0 += NU) {
+            PartialBatch<BF16, D, BS, NU> pbi;
+            pbi.load(part_o, part_ml, base, i0, npre, j);
+            pbi.add(S, min(npre - i0, NU));
+        }
+    };
+    if (start < end)  // one table chunk: end - start <= PS <= kTableChunk * BS
+        attend_chunk<BF16, D, BS>(S, qr, kbase, vbase, blk_bytes, trow, num_blocks, start, end, L, lane, n, j,
+                                  scale_log2, fold);
+    else
+        fold();
+    store_out<BF16, D, BS>(out_, row0, S, n, j, G);
 }
 
-// One wave per output row (request b, query head h), four rows per
-// workgroup: merges the request's prefix partials [0, npre) and its own
-// partials [P_pre, P_pre + nsuf).  Lane i holds partial i's (m, l) of the
-// current 64-partial window; each lane accumulates D / 64 dims, four
-// partials' loads in flight at a time.
-template <bool BF16, int D, int BS>
-__global__ __launch_bounds__(256) void merge_shared_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml,
-                                                           const int32_t* __restrict__ lens,
-                                                           const int32_t* __restrict__ prefix_blocks,
-                                                           void* __restrict__ out_, int B, int Hq, int max_blocks,
-                                                           int max_pre, int PS, int P_pre, int P_max) {
-    constexpr int PER = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (int64_t)B * Hq) return;
-    const int b = (int)(row / Hq);
-    const int L = lens[b];
-    const int pb = prefix_blocks[b];
-    const bool ok = L > 0 && (int64_t)L <= (int64_t)max_blocks * BS && pb >= 0 && pb <= max_pre &&
-                    shared_tokens<BS>(pb) <= L;
-    float res[PER];
-    if (!ok) {
-        // empty request: zero row; a length or prefix the table cannot hold: NaN row
-#pragma unroll
-        for (int e = 0; e < PER; ++e) res[e] = L <= 0 ? 0.0f : __builtin_nanf("");
-    } else {
-        const int T = shared_tokens<BS>(pb);
-        const int npre = (T + PS - 1) / PS;
-        const int np = npre + (L - T + PS - 1) / PS;
-        const float* ml = part_ml + row * P_max * 2;
-        const float* po = part_o + row * P_max * D + lane * PER;
-        auto slot = [&](int i) { return i < npre ? i : P_pre + (i - npre); };
-        float M = -INFINITY;
-        for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[2 * slot(i)]);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-        float num[PER];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) num[e] = 0.f;
-        float den = 0.f;
-        for (int w0 = 0; w0 < np; w0 += 64) {
-            const int nw = min(64, np - w0);
-            float wl = 0.f;
-            if (lane < nw) {
-                const int si = slot(w0 + lane);
-                wl = ml[2 * si + 1] * __builtin_amdgcn_exp2f(ml[2 * si] - M);
-            }
-            den += wl;
-            for (int i0 = 0; i0 < nw; i0 += 4) {
-                float v[4][PER];
-                float wt[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int i = min(i0 + u, nw - 1);  // past the end: a valid slot, weight 0
-                    const float* src = po + (int64_t)slot(w0 + i) * D;
-#pragma unroll
-                    for (int e = 0; e < PER; ++e) v[u][e] = src[e];
-                    const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
-                    wt[u] = (i0 + u < nw) ? wi : 0.0f;
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int e = 0; e < PER; ++e) num[e] += wt[u] * v[u][e];
-            }
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) den += shfl_xor_f(den, o);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) res[e] = num[e] / den;
-    }
-    if constexpr (BF16) {
-        uint16_t* o = reinterpret_cast<uint16_t*>(out_) + row * D + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] = (uint16_t)bf16_bits_rne(res[e]);
-    } else {
-        float* o = reinterpret_cast<float*>(out_) + row * D + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] = res[e];
-    }
+// Clears the suffix kernel's merge counters when no prefix kernel runs (a
+// fill kernel rather than a memset, so that a caller capturing the stream
+// into a graph records a kernel node).
+__global__ __launch_bounds__(256) void clear_counters_kernel(int32_t* __restrict__ c, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) c[i] = 0;
 }
 
 }  // namespace pa
@@ -302,6 +369,7 @@ struct SharedLaunch {
     const int32_t *tables, *lens, *groups, *pblk;
     void* out;
     float *po, *pml;
+    int32_t* counters;  // one per (request, kv-head)
     int B, Hq, Hkv, max_blocks, max_pre, num_blocks, num_groups, max_group, PS, P_pre, P_max;
     float sl2;
     hipStream_t s;
@@ -312,8 +380,8 @@ hipError_t launch_prefix(const SharedLaunch& a) {
     if (a.P_pre == 0 || a.num_groups == 0) return hipSuccess;
     hipLaunchKernelGGL((pa::decode_prefix_kernel<BF16, D, BS, NCT>),
                        dim3((unsigned)a.Hkv, (unsigned)a.P_pre, (unsigned)a.num_groups), dim3(64), 0, a.s, a.q, a.kc,
-                       a.vc, a.tables, a.groups, a.pblk, a.po, a.pml, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.max_blocks,
-                       a.max_pre, a.num_blocks, a.max_group, a.PS, a.P_max, a.sl2);
+                       a.vc, a.tables, a.groups, a.pblk, a.po, a.pml, a.counters, a.B * a.Hkv, a.B, a.Hq, a.Hkv,
+                       a.Hq / a.Hkv, a.max_blocks, a.max_pre, a.num_blocks, a.max_group, a.PS, a.P_max, a.sl2);
     return hipGetLastError();
 }
 
@@ -334,14 +402,19 @@ hipError_t launch_shared(const SharedLaunch& a) {
         e = launch_prefix<BF16, D, BS, max_columns(BF16, D) / 16>(a);
     if (e != hipSuccess) return e;
     const int P_suf = a.P_max - a.P_pre;
+    if (P_suf > 1 && (a.P_pre == 0 || a.num_groups == 0)) {
+        // no prefix launch to clear the counters (needed only when a request's
+        // own tokens can span several partitions)
+        const int nc = a.B * a.Hkv;
+        hipLaunchKernelGGL(pa::clear_counters_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, a.s,
+                           a.counters, nc);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((pa::decode_suffix_kernel<BF16, D, BS>), dim3((unsigned)a.Hkv, (unsigned)a.B, (unsigned)P_suf),
-                       dim3(64), 0, a.s, a.q, a.kc, a.vc, a.tables, a.lens, a.pblk, a.po, a.pml, a.Hq, a.Hkv,
-                       a.Hq / a.Hkv, a.max_blocks, a.max_pre, a.num_blocks, a.PS, a.P_pre, a.P_max, a.sl2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t rows = (int64_t)a.B * a.Hq;
-    hipLaunchKernelGGL((pa::merge_shared_kernel<BF16, D, BS>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, a.s,
-                       a.po, a.pml, a.lens, a.pblk, a.out, a.B, a.Hq, a.max_blocks, a.max_pre, a.PS, a.P_pre, a.P_max);
+                       dim3(64), 0, a.s, a.q, a.kc, a.vc, a.tables, a.lens, a.pblk, a.po, a.pml, a.counters, a.out,
+                       a.Hq, a.Hkv, a.Hq / a.Hkv, a.max_blocks, a.max_pre, a.num_blocks, a.PS, a.P_pre, a.P_max,
+                       a.sl2);
     return hipGetLastError();
 }
 
@@ -364,10 +437,11 @@ extern "C" size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int3
         return 0;
     const SharedPlan pl = shared_plan(block_size, max_blocks_per_seq, max_prefix_blocks, partition_size);
     const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)pl.p_max;
-    // [pa_decode's counter region, left untouched | partials o | partials (m, l)]:
+    // [pa_decode's counter region, left untouched | partials o | partials (m, l) |
+    //  merge counters, one per (request, kv-head) <= num_q_heads per request]:
     // the same workspace can then serve pa_decode's balanced split as well
     return pa_decode_counter_bytes() + align_up(rows * head_dim * sizeof(float)) +
-           align_up(rows * 2 * sizeof(float));
+           align_up(rows * 2 * sizeof(float)) + align_up((size_t)num_seqs * num_q_heads * sizeof(int32_t));
 }
 
 extern "C" pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
@@ -422,6 +496,8 @@ extern "C" pa_status pa_decode_shared_prefix(const void* q, const void* k_cache,
     char* parts = reinterpret_cast<char*>(workspace) + pa_decode_counter_bytes();
     a.po = reinterpret_cast<float*>(parts);
     a.pml = reinterpret_cast<float*>(parts + align_up(rows * head_dim * sizeof(float)));
+    a.counters = reinterpret_cast<int32_t*>(parts + align_up(rows * head_dim * sizeof(float)) +
+                                            align_up(rows * 2 * sizeof(float)));
     a.B = num_seqs;
     a.Hq = num_q_heads;
     a.Hkv = num_kv_heads;

@@ -364,10 +364,11 @@ def test_shared_prefix_max_group():
 def test_shared_prefix_workspace_size():
     cnt = _l().pa_decode_counter_bytes()
     # prefix: 30 blocks of 16 = 480 tokens -> 1 partition; own part: 640 tokens -> 2 partitions;
-    # the partials sit after pa_decode's (untouched) counter region
+    # the partials sit after pa_decode's (untouched) counter region, then one merge counter
+    # per (request, kv-head), at most one per query head
     n = pa.decode_shared_prefix_workspace_bytes(16, 32, 128, 16, 40, 30, 512)
     rows = 16 * 32 * 3
-    assert n >= cnt + rows * 128 * 4 + rows * 2 * 4 and n % 256 == 0
+    assert n >= cnt + rows * 128 * 4 + rows * 2 * 4 + 16 * 32 * 4 and n % 256 == 0
     assert pa.decode_shared_prefix_workspace_bytes(16, 32, 128, 16, 40, 41, 512) == 0
     assert pa.decode_shared_prefix_workspace_bytes(16, 32, 128, 16, 40, 30, 0) == 0
 

@@ -121,16 +121,18 @@ def test_full_size_every_row(name, ps):
 
 @pytest.mark.timeout(900)
 def test_full_size_shared_prefix_every_row():
-    """The shared-prefix decode at the prefix-sharing workload's full size, as the benchmark launches it."""
+    """The shared-prefix decode at the prefix-sharing workload's full size, with the
+    benchmark's 1024-token partitions and with 512-token ones."""
     w = make_workload("prefix_share", seed=0)
-    dev = build_device_batch(w, partition_size=512)
+    dev = build_device_batch(w, partition_size=1024)
     dev.cache_append()
     plan = dev.shared_plan()
     say("prefix_share shared: groups", plan.num_groups, "max group", plan.max_group, "prefix blocks",
         plan.max_prefix_blocks)
     assert plan.num_groups == 32 and plan.max_group == 8 and plan.max_prefix_blocks == 127
-    got = decode_output(dev.attend_shared(plan, partition_size=512))
-    check_rows(w, got, "prefix_share shared-prefix decode")
+    for ps in (1024, 512):
+        got = decode_output(dev.attend_shared(plan, partition_size=ps))
+        check_rows(w, got, f"prefix_share shared-prefix decode, partitions of {ps}")
     w.drop_kv()
 
 

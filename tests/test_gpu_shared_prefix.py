@@ -55,7 +55,7 @@ def check(got, ref, dtype, what, rows=None):
 
 # (label, prefix_share keywords, partition sizes)
 CASES = [
-    ("bf16-G4-bs16", dict(prompts=3, samples=8, prompt_len=300, tail_max=70), (64, 256, 512)),
+    ("bf16-G4-bs16", dict(prompts=3, samples=8, prompt_len=300, tail_max=70), (64, 256, 512, 1024)),
     ("bf16-G4-bs8", dict(prompts=2, samples=8, prompt_len=333, tail_max=50, block_size=8), (64, 512)),
     ("bf16-G4-bs32", dict(prompts=2, samples=6, prompt_len=1000, tail_max=90, block_size=32), (64, 512)),
     ("bf16-G8-bs16", dict(prompts=2, samples=8, prompt_len=515, tail_max=40, num_q_heads=64), (128, 512)),
