@@ -122,11 +122,15 @@ def test_partial_groupings_and_workspace_reuse():
     out = dev.attend_shared(part, partition_size=256)
     torch.cuda.synchronize()
     check(out_f64(out), ref, w.dtype, "two of four groups")
-    # an empty plan is the plain split decode
+    # an empty plan is the plain split decode; with no prefix launch a fill
+    # kernel clears the merge counters, so a second call on the same
+    # workspace (rows of two 256-token partitions) must agree as well
     none = pa.SharedPrefixPlan(np.zeros((0, 2), np.int32), np.zeros(w.batch, np.int32), 1, 0).to("cuda")
-    out = dev.attend_shared(none, partition_size=256)
-    torch.cuda.synchronize()
-    check(out_f64(out), ref, w.dtype, "no groups")
+    assert int(w.seq_lens.max()) > 256
+    for call in range(2):
+        out = dev.attend_shared(none, partition_size=256)
+        torch.cuda.synchronize()
+        check(out_f64(out), ref, w.dtype, f"no groups, call {call}")
 
 
 def test_shared_prefix_error_rows_without_fault():
