@@ -119,9 +119,14 @@ __global__ __launch_bounds__(64) void decode_kernel(
 // Log-sum-exp merge of per-partition results: one 256-lane workgroup per
 // (query head, sequence).  A lane owns four consecutive head-dim elements of
 // one partition row at a time (D / 4 lanes per row, so 1024 / D rows side by
-// side) and takes four rows per loop trip with their loads issued together,
-// so a workgroup has up to 4096 / D partition rows in flight; the row
-// groups' sums meet in LDS.
+// side) and takes kMergeRows rows per loop trip with all their loads issued
+// together, so a workgroup has up to kMergeRows * 1024 / D partition rows in
+// flight (all of a 512-token split of 131,072 tokens at D = 128 in two
+// trips).  Each row group keeps its own running maximum (rescaling its sums
+// when a trip raises it), so no pass over the maxima comes first; the row
+// groups' (maximum, sum, weighted output) meet in LDS.
+constexpr int kMergeRows = 16;
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
@@ -139,51 +144,59 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     const float* ml = part_ml + row * P_max * 2;
     const float* po = part_o + row * P_max * D;
     const int t = threadIdx.x;
-    const int lane = t & 63;
     const int rg = t / LPR;
     const int c = t % LPR;
 
-    float M = -INFINITY;
-    for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[2 * i]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-
+    float m = -INFINITY;  // this row group's running maximum
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    int i = rg;
-    for (; i + 3 * RG < np; i += 4 * RG) {
-        float2 w[4];
-        f32x4 o[4];
+    for (int i0 = rg; i0 < np; i0 += kMergeRows * RG) {
+        float2 w[kMergeRows];
+        f32x4 o[kMergeRows];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            w[u] = *reinterpret_cast<const float2*>(ml + 2 * (i + u * RG));
-            o[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(i + u * RG) * D + 4 * c);
+        for (int u = 0; u < kMergeRows; ++u) {
+            const int i = min(i0 + u * RG, np - 1);  // past the last partition: a valid row, skipped below
+            w[u] = *reinterpret_cast<const float2*>(ml + 2 * i);
+            o[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)i * D + 4 * c);
         }
+        float tm = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float wt = w[u].y * __builtin_amdgcn_exp2f(w[u].x - M);
-            den += wt;
-            num += wt * o[u];
+        for (int u = 0; u < kMergeRows; ++u)
+            if (i0 + u * RG < np) tm = fmaxf(tm, w[u].x);
+        const float mn = fmaxf(m, tm);
+        const float a = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+        den *= a;
+        num *= a;
+        m = mn;
+#pragma unroll
+        for (int u = 0; u < kMergeRows; ++u) {
+            if (i0 + u * RG < np) {
+                const float wt = w[u].y * __builtin_amdgcn_exp2f(w[u].x - m);
+                den += wt;
+                num += wt * o[u];
+            }
         }
-    }
-    for (; i < np; i += RG) {
-        const float2 w = *reinterpret_cast<const float2*>(ml + 2 * i);
-        const float wt = w.y * __builtin_amdgcn_exp2f(w.x - M);
-        den += wt;
-        num += wt * *reinterpret_cast<const f32x4*>(po + (int64_t)i * D + 4 * c);
     }
     __shared__ f32x4 s_num[RG][LPR];
-    __shared__ float s_den[RG];
+    __shared__ float s_den[RG], s_m[RG];
     s_num[rg][c] = num;
-    if (c == 0) s_den[rg] = den;
+    if (c == 0) {
+        s_den[rg] = den;
+        s_m[rg] = m;
+    }
     __syncthreads();
     if (t < LPR) {
-        f32x4 v = s_num[0][t];
-        float total = s_den[0];
+        float M = s_m[0];
 #pragma unroll
-        for (int r = 1; r < RG; ++r) {
-            v += s_num[r][t];
-            total += s_den[r];
+        for (int r = 1; r < RG; ++r) M = fmaxf(M, s_m[r]);
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        float total = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            // a row group with no partition (np < RG) has m = -inf and zero sums
+            const float f = s_m[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s_m[r] - M);
+            v += f * s_num[r][t];
+            total += f * s_den[r];
         }
         v = v / total;
         if constexpr (BF16) {
