@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void cache_write_bulk_kernel(const char* __res
         for (int p = tid; p < C::PIECES; p += 256) {
             // keys [D/X][BS][X]: piece p = (chunk p / BS, token p % BS)
             const int c = p / BS, off = p % BS;
-            st16(kc + tile + (int64_t)p * 16, *reinterpret_cast<const u32x4*>(lk + (j + off) * C::RS + c * 16));
+            st16_stream(kc + tile + (int64_t)p * 16, *reinterpret_cast<const u32x4*>(lk + (j + off) * C::RS + c * 16));
             // values [D][BS]: piece p = (row p / PR, positions X (p % PR) ..)
             const int d = p / C::PR, pos0 = (p % C::PR) * C::X;
             u32x4 out;
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void cache_write_bulk_kernel(const char* __res
 #pragma unroll
                 for (int e = 0; e < 4; ++e) out[e] = *reinterpret_cast<const uint32_t*>(lv + (j + pos0 + e) * C::RS + d * 4);
             }
-            st16(vc + tile + (int64_t)p * 16, out);
+            st16_stream(vc + tile + (int64_t)p * 16, out);
         }
     }
 

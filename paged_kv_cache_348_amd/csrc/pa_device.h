@@ -26,6 +26,12 @@ __device__ __forceinline__ u32x2 ld8_stream(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
+// 16-byte streaming store: marked non-temporal, for pool tiles written once
+// and not read again soon.
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // float -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     uint32_t u = __float_as_uint(f);
