@@ -119,15 +119,48 @@ __global__ __launch_bounds__(64) void decode_kernel(
 // Log-sum-exp merge of per-partition results: one 256-lane workgroup per
 // (query head, sequence).  A lane owns four consecutive head-dim elements of
 // one partition row at a time (D / 4 lanes per row, so 1024 / D rows side by
-// side) and takes kMergeRows rows per loop trip with all their loads issued
-// together, so a workgroup has up to kMergeRows * 1024 / D partition rows in
-// flight (all of a 512-token split of 131,072 tokens at D = 128 in two
-// trips).  Each row group keeps its own running maximum (rescaling its sums
-// when a trip raises it), so no pass over the maxima comes first; the row
-// groups' (maximum, sum, weighted output) meet in LDS.
-constexpr int kMergeRows = 16;
+// side) and takes NR rows per loop trip with all their loads issued
+// together.  The launch picks NR from the partition bound: 16 when rows can
+// have many partitions (a 512-token split of 131,072 tokens at D = 128 in
+// two trips; few, long workgroups), 4 or 1 when they have few (many short
+// workgroups, which need the smaller register count to share a CU, and
+// loads past the last partition would only repeat it).  Each
+// row group keeps its own running maximum (rescaling its sums when a trip
+// raises it), so no pass over the maxima comes first; the row groups'
+// (maximum, sum, weighted output) meet in LDS.
+template <int NR, int D>
+__device__ __forceinline__ void merge_trips(const float* __restrict__ ml, const float* __restrict__ po, int np,
+                                            int rg, int c, int RG, float& m, float& den, f32x4& num) {
+    for (int i0 = rg; i0 < np; i0 += NR * RG) {
+        float2 w[NR];
+        f32x4 o[NR];
+#pragma unroll
+        for (int u = 0; u < NR; ++u) {
+            const int i = min(i0 + u * RG, np - 1);  // past the last partition: a valid row, skipped below
+            w[u] = *reinterpret_cast<const float2*>(ml + 2 * i);
+            o[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)i * D + 4 * c);
+        }
+        float tm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < NR; ++u)
+            if (i0 + u * RG < np) tm = fmaxf(tm, w[u].x);
+        const float mn = fmaxf(m, tm);
+        const float a = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+        den *= a;
+        num *= a;
+        m = mn;
+#pragma unroll
+        for (int u = 0; u < NR; ++u) {
+            if (i0 + u * RG < np) {
+                const float wt = w[u].y * __builtin_amdgcn_exp2f(w[u].x - m);
+                den += wt;
+                num += wt * o[u];
+            }
+        }
+    }
+}
 
-template <bool BF16, int D>
+template <bool BF16, int D, int NR>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     const int32_t* __restrict__ lens, void* __restrict__ out_,
@@ -150,33 +183,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     float m = -INFINITY;  // this row group's running maximum
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int i0 = rg; i0 < np; i0 += kMergeRows * RG) {
-        float2 w[kMergeRows];
-        f32x4 o[kMergeRows];
-#pragma unroll
-        for (int u = 0; u < kMergeRows; ++u) {
-            const int i = min(i0 + u * RG, np - 1);  // past the last partition: a valid row, skipped below
-            w[u] = *reinterpret_cast<const float2*>(ml + 2 * i);
-            o[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)i * D + 4 * c);
-        }
-        float tm = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < kMergeRows; ++u)
-            if (i0 + u * RG < np) tm = fmaxf(tm, w[u].x);
-        const float mn = fmaxf(m, tm);
-        const float a = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
-        den *= a;
-        num *= a;
-        m = mn;
-#pragma unroll
-        for (int u = 0; u < kMergeRows; ++u) {
-            if (i0 + u * RG < np) {
-                const float wt = w[u].y * __builtin_amdgcn_exp2f(w[u].x - m);
-                den += wt;
-                num += wt * o[u];
-            }
-        }
-    }
+    merge_trips<NR, D>(ml, po, np, rg, c, RG, m, den, num);
     __shared__ f32x4 s_num[RG][LPR];
     __shared__ float s_den[RG], s_m[RG];
     s_num[rg][c] = num;
@@ -978,8 +985,17 @@ hipError_t launch_decode(const Launch& a) {
                        a.lens, a.out, a.po, a.pml, a.Hq, a.Hkv, G, a.max_blocks, a.num_blocks, a.PS, a.P_max, a.sl2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.P_max <= 1) return e;
-    hipLaunchKernelGGL((pa::merge_kernel<BF16, D>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(256), 0, a.stream, a.po,
-                       a.pml, a.lens, a.out, a.Hq, a.max_blocks, BS, a.PS, a.P_max);
+    constexpr int RG = 256 / (D / 4);  // partition rows a merge workgroup holds side by side
+    const dim3 mg((unsigned)a.Hq, (unsigned)a.B);
+    if (a.P_max <= RG)
+        hipLaunchKernelGGL((pa::merge_kernel<BF16, D, 1>), mg, dim3(256), 0, a.stream, a.po, a.pml, a.lens, a.out,
+                           a.Hq, a.max_blocks, BS, a.PS, a.P_max);
+    else if (a.P_max <= 4 * RG)
+        hipLaunchKernelGGL((pa::merge_kernel<BF16, D, 4>), mg, dim3(256), 0, a.stream, a.po, a.pml, a.lens, a.out,
+                           a.Hq, a.max_blocks, BS, a.PS, a.P_max);
+    else
+        hipLaunchKernelGGL((pa::merge_kernel<BF16, D, 16>), mg, dim3(256), 0, a.stream, a.po, a.pml, a.lens, a.out,
+                           a.Hq, a.max_blocks, BS, a.PS, a.P_max);
     return hipGetLastError();
 }
 
