@@ -411,50 +411,57 @@ __device__ __forceinline__ void flash_state_init(FlashState<D>& S) {
     for (int c = 0; c < D / 16; ++c) S.acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Online-softmax update and PV of one tile from its step scores: the
-// method of compute_step (base 2, lazy rescale), with the scale folded into
-// the exponent argument (scale_log2 > 0), the causal mask per lane column
-// (limit Lcol) on a tail step (tail: some column's limit falls inside the
-// step, a wave-uniform test), and the reference moved only when some lane
-// holds a score above its column's cached threshold (a ballot): most steps
-// take no cross-lane maximum and no cross-lane sum.  v: the step's values,
-// already zeroed at or past the keys' end.
-template <int D, int BS>
-__device__ __forceinline__ void flash_softmax_pv(FlashState<D>& S, f32x4 sa, f32x4 sb, const u32x4 (&v)[D / 16],
-                                                 int tok0, int j, float sl2, int Lcol, bool tail) {
-    float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-    if (tail) {
+// Online-softmax update and PV of all NCT tiles of a wave from their step
+// scores (already masked: -inf past each column's limit): the method of
+// compute_step (base 2, lazy rescale), with the scale folded into the
+// exponent argument (scale_log2 > 0).  The references move only when some
+// lane of some tile holds a score above its column's cached threshold (one
+// ballot per step for all tiles), so most steps take no cross-lane maximum
+// and no cross-lane sum; when one does, every tile moves its reference to
+// its running maximum (a move that lazy rescaling would have skipped is
+// still exact: the reference only has to keep the scores seen so far at
+// most kLazyRescale above it).  v: the step's values, already zeroed at or
+// past the keys' end.
+template <int D, int NCT>
+__device__ __forceinline__ void flash_softmax_pv_all(FlashState<D> (&S)[NCT], const float (&s)[NCT][8],
+                                                     const u32x4 (&v)[D / 16], float sl2) {
+    float lm[NCT];
+    bool up = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] = flash_tok<BS>(tok0, j, e) < Lcol ? s[e] : -INFINITY;
+    for (int t = 0; t < NCT; ++t) {
+        lm[t] = vmax3(vmax3(s[t][0], s[t][1], s[t][2]), vmax3(s[t][3], s[t][4], s[t][5]), vmax(s[t][6], s[t][7]));
+        up = up || lm[t] > S[t].thr;
     }
-    // the lane's largest score (scores are never NaN here, so plain v_max3 /
-    // v_max do; fmaxf would add canonicalising instructions)
-    const float lm = vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), vmax(s[6], s[7]));
-    if (__builtin_amdgcn_ballot_w64(lm > S.thr)) {
-        // the column maximum over its four lanes, then the rescale
-        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
-        float mx = vmax(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = vmax(__uint_as_float(r32[0]), __uint_as_float(r32[1])) * sl2;
-        const float m_new = vmax(S.m, mx);  // -inf stays -inf (a column with no visible key yet)
-        const float alpha = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(S.m - m_new);
-        S.l *= alpha;
+    if (__builtin_amdgcn_ballot_w64(up)) {
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) S.acc[c] *= alpha;
-        S.m = m_new;
-        S.thr = (m_new + kLazyRescale) / sl2;
-        S.negm = m_new == -INFINITY ? 0.0f : -m_new;
+        for (int t = 0; t < NCT; ++t) {
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lm[t]), __float_as_uint(lm[t]), false, false);
+            float mx = vmax(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = vmax(__uint_as_float(r32[0]), __uint_as_float(r32[1])) * sl2;
+            const float m_new = vmax(S[t].m, mx);
+            const float alpha = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(S[t].m - m_new);
+            S[t].l *= alpha;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) S[t].acc[c] *= alpha;
+            S[t].m = m_new;
+            S[t].thr = (m_new + kLazyRescale) / sl2;
+            S[t].negm = m_new == -INFINITY ? 0.0f : -m_new;
+        }
     }
-    float pe[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sl2, S.negm));
-    S.l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-    const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]), pack_bf16x2(pe[4], pe[5]),
-                      pack_bf16x2(pe[6], pe[7])};
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+    for (int t = 0; t < NCT; ++t) {
+        float pe[8];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-        S.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[c]), pb, S.acc[c], 0, 0, 0);
+        for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][e], sl2, S[t].negm));
+        S[t].l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+        const u32x4 pw = {pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3]), pack_bf16x2(pe[4], pe[5]),
+                          pack_bf16x2(pe[6], pe[7])};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            S[t].acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[c]), pb, S[t].acc[c], 0, 0, 0);
+    }
 }
 
 template <int D, int BS, int NW, int NCT>
@@ -477,6 +484,7 @@ struct FlashWave {
     float sl2;
     int bad;  // a table entry outside the pool was met (wave-uniform)
     int Lcol[NCT], Lmin[NCT];
+    int toff[8];  // step token of each score element, less the step's first token
     u32x4 qr[NCT][C::NKC];
     FlashState<D> S[NCT];
 
@@ -500,7 +508,7 @@ struct FlashWave {
 #pragma unroll
         for (int i = 0; i < F::NLD; ++i) {
             const bool ok = e[i] >= 0 && e[i] < num_blocks;
-            bad = __builtin_amdgcn_readfirstlane(bad | (ok ? 0 : 1));
+            bad |= ok ? 0 : 1;  // scalar: e[i] comes from a scalar load
             // wave-uniform piece base (scalar registers) + the lane's 16 bytes
             const uint64_t o = (uint64_t)(uint32_t)(ok ? e[i] : 0) * blk_bytes + (uint32_t)F::inner(w, i);
             const int lo = F::blk(w, i) * F::TSTRIDE + F::inner(w, i);
@@ -532,19 +540,37 @@ struct FlashWave {
             u32x4 v[C::NV];
             flash_read_values<D, BS, F::TSTRIDE>(v, slot_keys<SL>() + F::SLOT, off);
             const int tok0 = 32 * x;
-            if (tok0 + 32 > kend) {  // the last step: values at or past the keys' end may be anything
-                uint32_t keep[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    keep[q] = (flash_tok<BS>(tok0, j, 2 * q) < kend ? 0x0000ffffu : 0u) |
-                              (flash_tok<BS>(tok0, j, 2 * q + 1) < kend ? 0xffff0000u : 0u);
-#pragma unroll
-                for (int c = 0; c < C::NV; ++c)
-                    v[c] = u32x4{v[c][0] & keep[0], v[c][1] & keep[1], v[c][2] & keep[2], v[c][3] & keep[3]};
-            }
+            float sc[NCT][8];
 #pragma unroll
             for (int t = 0; t < NCT; ++t)
-                flash_softmax_pv<D, BS>(S[t], cur[t][0], cur[t][1], v, tok0, j, sl2, Lcol[t], tok0 + 32 > Lmin[t]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sc[t][e] = cur[t][0][e];
+                    sc[t][4 + e] = cur[t][1][e];
+                }
+            // One scalar test for every tail: Lmin[0] is the smallest key limit
+            // of the wave's columns and kend bounds them all, so a step with no
+            // limit inside it needs no mask and no value zeroing.  Masking a
+            // tile whose limits all lie past the step changes nothing.
+            if (tok0 + 32 > Lmin[0]) {
+                if (tok0 + 32 > kend) {  // the last step: values at or past the keys' end may be anything
+                    const int vl = kend - tok0;
+                    uint32_t keep[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        keep[q] = (toff[2 * q] < vl ? 0x0000ffffu : 0u) | (toff[2 * q + 1] < vl ? 0xffff0000u : 0u);
+#pragma unroll
+                    for (int c = 0; c < C::NV; ++c)
+                        v[c] = u32x4{v[c][0] & keep[0], v[c][1] & keep[1], v[c][2] & keep[2], v[c][3] & keep[3]};
+                }
+#pragma unroll
+                for (int t = 0; t < NCT; ++t) {
+                    const int lim = Lcol[t] - tok0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sc[t][e] = toff[e] < lim ? sc[t][e] : -INFINITY;
+                }
+            }
+            flash_softmax_pv_all<D, NCT>(S, sc, v, sl2);
         }
         // step x + 2's pieces have landed once at most step x + 3's (2 NLD
         // loads) are outstanding; the barrier makes every wave's visible and
@@ -647,6 +673,8 @@ void prefill_flash_kernel(const void* __restrict__ q_, const void* __restrict__ 
     W.j = W.lane >> 4;
     W.blk_bytes = (uint32_t)Hkv * C::TILE * C::ES;
     W.off.init(W.n, W.j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) W.toff[e] = flash_tok<BS>(0, W.j, e);
     W.kbase = reinterpret_cast<const char*>(kc_) + (int64_t)g * C::TILE * C::ES;
     W.vbase = reinterpret_cast<const char*>(vc_) + (int64_t)g * C::TILE * C::ES;
     W.trow = tables + (int64_t)b * max_blocks;
