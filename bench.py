@@ -376,6 +376,28 @@ def append_main(args, w):
     per_tok = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
     algo = 2 * T * per_tok  # read + write
     gbps = algo / (ms * 1e-3) / 1e9
+
+    # reference: a plain device copy of the same keys and values (the same
+    # bytes read and written, contiguous on both sides), timed the same way
+    ck, cv = torch.empty_like(kd), torch.empty_like(vd)
+
+    def copy():
+        ck.copy_(kd)
+        cv.copy_(vd)
+
+    for _ in range(args.warmup):
+        copy()
+    copy_runs = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            copy()
+        b.record(stream)
+        torch.cuda.synchronize()
+        copy_runs.append(a.elapsed_time(b) / args.steps)
+    ms_copy = float(np.median(copy_runs))
+    del ck, cv
     res = {
         "metric": "bulk cache append (pa_cache_write) tokens/s on 1 MI355X",
         "value": T / (ms * 1e-3), "unit": "appended tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -387,6 +409,9 @@ def append_main(args, w):
                      "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
                      "algorithmic_bytes_per_launch": algo},
         "runs_ms": runs,
+        "copy_same_bytes": {"what": "plain device copy of the same keys and values (read + write)",
+                            "ms": ms_copy, "gbps": algo / (ms_copy * 1e-3) / 1e9,
+                            "frac_of_8tbs": algo / (ms_copy * 1e-3) / 1e9 / HBM_PEAK_GBPS},
     }
     print(json.dumps(res), flush=True)
     return 0
