@@ -347,55 +347,76 @@ struct CutPiece {
     int t0, M;           // multi-token query: the segment's rows
 };
 
-// Count a piece in; the wave that brings the segment's counter to its
-// piece count merges every piece (log-sum-exp rule), writes the G rows and
-// puts the counter back to zero.
-template <bool BF16, int D, int BS, bool MULTI>
-__device__ __forceinline__ void count_in(const CutPiece& cp, const float* __restrict__ slot_o,
-                                         const float* __restrict__ slot_ml, int32_t* __restrict__ counters,
-                                         void* __restrict__ out_, int64_t S, int nw, int Hq, int Hkv, int G, int lane,
-                                         int n, int j) {
-    using C = DecodeCfg<BF16, D, BS>;
-    const int SC = MULTI ? 16 : G;              // columns per partial slot
-    const int ncol = MULTI ? cp.M * G : G;      // columns with an output row
+// The counter of a cut segment and the waves holding its pieces: one
+// counter per cut segment, named by the first wave holding a piece of it (a
+// wave is the first of at most one cut segment: the last one that starts in
+// it), so the names never collide, whatever the batch.
+struct CutCount {
+    int32_t* cnt;
+    int w0, w1;
+};
+__device__ __forceinline__ CutCount cut_count(const CutPiece& cp, int32_t* __restrict__ counters, int64_t S, int nw) {
     const int w0 = wave_of_step(cp.seg0, S, nw);
-    const int w1 = wave_of_step(cp.seg1 - 1, S, nw);
-    // One counter per cut segment, named by the first wave holding a piece
-    // of it: a wave is the first of at most one cut segment (the last one
-    // that starts in it), so the names never collide, whatever the batch.
-    int32_t* cnt = counters + w0;
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    if (old != w1 - w0) return;
-    if (n < ncol) {
-        float M = -INFINITY;
-        for (int k = w0; k <= w1; ++k) {
-            const int64_t sk = 2 * (int64_t)k + ((k == w0 && cp.seg0 != S * k / nw) ? 1 : 0);
-            M = fmaxf(M, coherent_load(reinterpret_cast<const uint64_t*>(slot_ml + (sk * SC + n) * 2)).x);
-        }
-        RunState<BF16, D, BS> Mg;
-        Mg.m = M;
-        Mg.l = 0.0f;
-        Mg.bad = false;
+    return CutCount{counters + w0, w0, wave_of_step(cp.seg1 - 1, S, nw)};
+}
+
+// Merge every piece of a cut segment (log-sum-exp rule) and write its rows:
+// the pieces' (m, l) and values are loaded two pieces at a time, all loads
+// of a pair in flight together, with a running maximum over the pairs
+// (a segment has two pieces unless it spans more than two waves).  Called
+// by the wave whose count-in completed the segment.
+template <bool BF16, int D, int BS, bool MULTI>
+__device__ __forceinline__ void merge_cut(const CutPiece& cp, const CutCount& cc, const float* __restrict__ slot_o,
+                                          const float* __restrict__ slot_ml, void* __restrict__ out_, int64_t S, int nw,
+                                          int Hq, int G, int n, int j) {
+    using C = DecodeCfg<BF16, D, BS>;
+    const int SC = MULTI ? 16 : G;          // columns per partial slot
+    const int ncol = MULTI ? cp.M * G : G;  // columns with an output row
+    if (n >= ncol) return;
+    RunState<BF16, D, BS> Mg;
+    Mg.m = -INFINITY;
+    Mg.l = 0.0f;
+    Mg.bad = false;
 #pragma unroll
-        for (int c = 0; c < C::NV; ++c) Mg.acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k = w0; k <= w1; ++k) {
-            const int64_t sk = 2 * (int64_t)k + ((k == w0 && cp.seg0 != S * k / nw) ? 1 : 0);
-            const float2 ml = coherent_load(reinterpret_cast<const uint64_t*>(slot_ml + (sk * SC + n) * 2));
-            const float wt = __builtin_amdgcn_exp2f(ml.x - M);
-            Mg.l += wt * ml.y;
+    for (int c = 0; c < C::NV; ++c) Mg.acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the first wave's piece sits in its second slot when the segment starts
+    // inside that wave (the other waves' pieces begin their ranges)
+    const int first_slot = cp.seg0 != S * cc.w0 / nw ? 1 : 0;
+    for (int k0 = cc.w0; k0 <= cc.w1; k0 += 2) {
+        float2 ml[2];
+        f32x4 o[2][C::NV];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int k = min(k0 + u, cc.w1);  // a lone last piece loads twice, counted once
+            const int64_t sk = 2 * (int64_t)k + (k == cc.w0 ? first_slot : 0);
+            ml[u] = coherent_load(reinterpret_cast<const uint64_t*>(slot_ml + (sk * SC + n) * 2));
             const uint64_t* po = reinterpret_cast<const uint64_t*>(slot_o + (sk * SC + n) * D);
 #pragma unroll
             for (int c = 0; c < C::NV; ++c) {
                 const int e = (16 * c + 4 * j) / 2;
                 const float2 lo = coherent_load(po + e), hi = coherent_load(po + e + 1);
-                Mg.acc[c] += wt * f32x4{lo.x, lo.y, hi.x, hi.y};
+                o[u][c] = f32x4{lo.x, lo.y, hi.x, hi.y};
             }
         }
-        store_out<BF16, D, BS>(out_, col_row<MULTI>(cp.b, cp.g, cp.t0, n, Hq, G) - n, Mg, n, j, ncol);
+        const bool two = k0 + 1 <= cc.w1;
+        const float mb = two ? fmaxf(ml[0].x, ml[1].x) : ml[0].x;
+        if (mb > Mg.m) {  // every piece has a visible key, so mb is finite
+            const float alpha = Mg.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mg.m - mb);
+            Mg.l *= alpha;
+#pragma unroll
+            for (int c = 0; c < C::NV; ++c) Mg.acc[c] *= alpha;
+            Mg.m = mb;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (u == 1 && !two) break;
+            const float wt = __builtin_amdgcn_exp2f(ml[u].x - Mg.m);
+            Mg.l += wt * ml[u].y;
+#pragma unroll
+            for (int c = 0; c < C::NV; ++c) Mg.acc[c] += wt * o[u][c];
+        }
     }
-    if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_out<BF16, D, BS>(out_, col_row<MULTI>(cp.b, cp.g, cp.t0, n, Hq, G) - n, Mg, n, j, ncol);
 }
 
 // Finish the piece whose last step was just computed: a whole segment is
@@ -840,13 +861,31 @@ __global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_balanced_k
     }
     const CutPiece cut0 = W.cut0, cut1 = W.cut1;
 
-    // 5. count the cut pieces in (their partials must be at the coherent level first)
+    // 5. count the cut pieces in (their partials must be at the coherent
+    //    level first), both counts in one round trip; the wave that completes
+    //    a segment's count merges its pieces and puts the counter back to zero
     if (cut0.valid || cut1.valid) {
         __builtin_amdgcn_s_waitcnt(0);
-        if (cut0.valid)
-            count_in<BF16, D, BS, MULTI>(cut0, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
-        if (cut1.valid)
-            count_in<BF16, D, BS, MULTI>(cut1, slot_o, slot_ml, counters, out_, S, nw, Hq, Hkv, G, lane, n, j);
+        const CutCount k0 = cut_count(cut0, counters, S, nw), k1 = cut_count(cut1, counters, S, nw);
+        int old0 = -1, old1 = -1;
+        if (lane == 0) {
+            if (cut0.valid) old0 = __hip_atomic_fetch_add(k0.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (cut1.valid) old1 = __hip_atomic_fetch_add(k1.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        old0 = __shfl(old0, 0, 64);
+        old1 = __shfl(old1, 0, 64);
+        const bool mine0 = cut0.valid && old0 == k0.w1 - k0.w0;
+        const bool mine1 = cut1.valid && old1 == k1.w1 - k1.w0;
+        // one copy of the merge (two inlined copies raised the kernel's
+        // register count past the main loop's)
+#pragma unroll 1
+        for (int q = 0; q < 2; ++q) {
+            if (!(q == 0 ? mine0 : mine1)) continue;
+            const CutPiece cp = q == 0 ? cut0 : cut1;
+            const CutCount kq = q == 0 ? k0 : k1;
+            merge_cut<BF16, D, BS, MULTI>(cp, kq, slot_o, slot_ml, out_, S, nw, Hq, G, n, j);
+            if (lane == 0) __hip_atomic_store(kq.cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     // 6. the new tokens' stores, last: nothing in the launch waits for them
     if constexpr (APPEND) append_rows<C::ES, D, BS>(ap, w, nwaves, B * Hkv, Hkv, lane);
