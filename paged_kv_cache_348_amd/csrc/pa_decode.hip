@@ -876,8 +876,7 @@ __global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_balanced_k
         old1 = __shfl(old1, 0, 64);
         const bool mine0 = cut0.valid && old0 == k0.w1 - k0.w0;
         const bool mine1 = cut1.valid && old1 == k1.w1 - k1.w0;
-        // one copy of the merge (two inlined copies raised the kernel's
-        // register count past the main loop's)
+        // one inlined copy of the merge serves both cut pieces
 #pragma unroll 1
         for (int q = 0; q < 2; ++q) {
             if (!(q == 0 ? mine0 : mine1)) continue;
